@@ -1,0 +1,14 @@
+"""fp64 CPU oracle for causal grouped-query attention (test infrastructure only).
+
+Only the tests, the package smoke check and the bench's CPU-baseline leg may
+import this package.  The HIP library never uses it.
+"""
+from .oracle import (  # noqa: F401
+    OracleLib,
+    attn_fwd,
+    attn_probs,
+    attn_rows,
+    build,
+    load,
+    threads,
+)

@@ -1,0 +1,158 @@
+"""ctypes wrapper around the plain-C fp64 attention oracle (attn_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the package smoke check and the bench's
+CPU-baseline leg use it; the HIP path never does.
+
+Inputs are numpy arrays holding exactly the values the GPU receives:
+float32 arrays for fp32 runs, or uint16 arrays carrying bf16 bit patterns.
+Outputs are float64.  See attn_oracle.c for the definition computed.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+HERE = Path(__file__).resolve().parent
+SOURCE = HERE / "attn_oracle.c"
+LIBRARY = HERE / "liboracle_attn.so"
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+_c_double_p = ctypes.POINTER(ctypes.c_double)
+_c_int64_p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(source: Path = SOURCE, output: Path = LIBRARY) -> Path:
+    """Compile the oracle with gcc (plain -O2, OpenMP) into a shared library."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           str(source), "-o", str(output) + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(str(output) + ".tmp", output)
+    return output
+
+
+class OracleLib:
+    """One loaded copy of the oracle library (the tests also load mutants)."""
+
+    def __init__(self, path: Path):
+        self.path = Path(path)
+        lib = ctypes.CDLL(str(self.path))
+        common = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_double]
+        lib.tessera_oracle_attn_fwd.argtypes = common + [_c_double_p, _c_double_p, ctypes.c_int]
+        lib.tessera_oracle_attn_fwd.restype = ctypes.c_int
+        lib.tessera_oracle_attn_rows.argtypes = common + [
+            _c_int64_p, ctypes.c_int64, _c_double_p, _c_double_p, ctypes.c_int]
+        lib.tessera_oracle_attn_rows.restype = ctypes.c_int
+        lib.tessera_oracle_attn_probs.argtypes = common + [_c_double_p, _c_double_p, _c_double_p]
+        lib.tessera_oracle_attn_probs.restype = ctypes.c_int
+        lib.tessera_oracle_threads.argtypes = [ctypes.c_int]
+        lib.tessera_oracle_threads.restype = ctypes.c_int
+        self.lib = lib
+
+    # -- helpers -----------------------------------------------------------
+    @staticmethod
+    def _prep(q, k, v):
+        arrs = [np.ascontiguousarray(a) for a in (q, k, v)]
+        dt = arrs[0].dtype
+        if any(a.dtype != dt for a in arrs):
+            raise ValueError("q, k and v must share one dtype")
+        if dt == np.float32:
+            code = DTYPE_F32
+        elif dt == np.uint16:
+            code = DTYPE_BF16
+        else:
+            raise ValueError(f"oracle takes float32 or uint16 (bf16 bits), got {dt}")
+        if arrs[0].ndim != 4 or arrs[1].ndim != 4 or arrs[2].ndim != 4:
+            raise ValueError("q, k, v must be 4-D [B, H, T, D]")
+        B, Hq, T, D = arrs[0].shape
+        if arrs[1].shape != arrs[2].shape or arrs[1].shape[0] != B or \
+                arrs[1].shape[2] != T or arrs[1].shape[3] != D:
+            raise ValueError("k and v must be [B, Hkv, T, D] matching q")
+        Hkv = arrs[1].shape[1]
+        return arrs, code, (B, Hq, Hkv, T, D)
+
+    @staticmethod
+    def _ptr(a):
+        return a.ctypes.data_as(ctypes.c_void_p)
+
+    @staticmethod
+    def _check(rc, name):
+        if rc != 0:
+            raise RuntimeError(f"{name} failed with code {rc}")
+
+    # -- entry points ------------------------------------------------------
+    def attn_fwd(self, q, k, v, causal: bool, scale: float, nthreads: int = 0):
+        (q, k, v), code, (B, Hq, Hkv, T, D) = self._prep(q, k, v)
+        O = np.empty((B, Hq, T, D), np.float64)
+        lse = np.empty((B, Hq, T), np.float64)
+        rc = self.lib.tessera_oracle_attn_fwd(
+            self._ptr(q), self._ptr(k), self._ptr(v), code, B, Hq, Hkv, T, D,
+            int(bool(causal)), float(scale),
+            O.ctypes.data_as(_c_double_p), lse.ctypes.data_as(_c_double_p), int(nthreads))
+        self._check(rc, "tessera_oracle_attn_fwd")
+        return O, lse
+
+    def attn_rows(self, q, k, v, causal: bool, scale: float, rows, nthreads: int = 0):
+        """rows: flat indices (b*Hq + h)*T + i.  Returns O [n, D], lse [n]."""
+        (q, k, v), code, (B, Hq, Hkv, T, D) = self._prep(q, k, v)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows.shape[0]
+        O = np.empty((n, D), np.float64)
+        lse = np.empty((n,), np.float64)
+        rc = self.lib.tessera_oracle_attn_rows(
+            self._ptr(q), self._ptr(k), self._ptr(v), code, B, Hq, Hkv, T, D,
+            int(bool(causal)), float(scale), rows.ctypes.data_as(_c_int64_p), n,
+            O.ctypes.data_as(_c_double_p), lse.ctypes.data_as(_c_double_p), int(nthreads))
+        self._check(rc, "tessera_oracle_attn_rows")
+        return O, lse
+
+    def attn_probs(self, q, k, v, causal: bool, scale: float):
+        (q, k, v), code, (B, Hq, Hkv, T, D) = self._prep(q, k, v)
+        O = np.empty((B, Hq, T, D), np.float64)
+        lse = np.empty((B, Hq, T), np.float64)
+        P = np.empty((B, Hq, T, T), np.float64)
+        rc = self.lib.tessera_oracle_attn_probs(
+            self._ptr(q), self._ptr(k), self._ptr(v), code, B, Hq, Hkv, T, D,
+            int(bool(causal)), float(scale), O.ctypes.data_as(_c_double_p),
+            lse.ctypes.data_as(_c_double_p), P.ctypes.data_as(_c_double_p))
+        self._check(rc, "tessera_oracle_attn_probs")
+        return O, lse, P
+
+    def threads(self, nthreads: int = 0) -> int:
+        return int(self.lib.tessera_oracle_threads(int(nthreads)))
+
+
+_DEFAULT: OracleLib | None = None
+
+
+def load() -> OracleLib:
+    """The oracle built from attn_oracle.c (compiled on first use if absent)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        if not LIBRARY.exists() or LIBRARY.stat().st_mtime < SOURCE.stat().st_mtime:
+            build()
+        _DEFAULT = OracleLib(LIBRARY)
+    return _DEFAULT
+
+
+def attn_fwd(q, k, v, causal, scale, nthreads=0):
+    return load().attn_fwd(q, k, v, causal, scale, nthreads)
+
+
+def attn_rows(q, k, v, causal, scale, rows, nthreads=0):
+    return load().attn_rows(q, k, v, causal, scale, rows, nthreads)
+
+
+def attn_probs(q, k, v, causal, scale):
+    return load().attn_probs(q, k, v, causal, scale)
+
+
+def threads(nthreads=0):
+    return load().threads(nthreads)

@@ -1,0 +1,51 @@
+"""CPU tests of the seeded synthetic input generator."""
+import numpy as np
+import torch
+
+from attention_flashattention_fwd_amd import inputs
+
+
+def test_draws_are_seeded_and_ordered():
+    q1, k1, v1 = inputs.draw_fp32(1, 2, 1, 8, 4, seed=0)
+    q2, k2, v2 = inputs.draw_fp32(1, 2, 1, 8, 4, seed=0)
+    assert np.array_equal(q1, q2) and np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    rng = np.random.default_rng(0)
+    assert np.array_equal(q1, rng.standard_normal((1, 2, 8, 4), dtype=np.float32))
+    assert np.array_equal(k1, rng.standard_normal((1, 1, 8, 4), dtype=np.float32))
+    q3, _, _ = inputs.draw_fp32(1, 2, 1, 8, 4, seed=1)
+    assert not np.array_equal(q1, q3)
+
+
+def test_bf16_cast_is_round_to_nearest_even():
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5], np.float32)
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    b = inputs.bits(t)
+    assert b.dtype == np.uint16
+    # ties go to even: 1+2^-8 -> 1.0 ; 1+3*2^-8 -> 1+2^-6 (0x3F82)
+    assert list(b) == [0x3F80, 0x3F80, 0x3F82, 0xC020]
+
+
+def test_element_outliers_fraction():
+    q, k, _ = inputs.draw_fp32(2, 4, 2, 512, 64, seed=0, outliers="elements")
+    q0, k0, _ = inputs.draw_fp32(2, 4, 2, 512, 64, seed=0)
+    ratio_q = (q != q0).mean()
+    assert 0.008 < ratio_q < 0.012
+    changed = q != q0
+    assert np.array_equal(q[changed], q0[changed] * 8)
+    assert 0.008 < (k != k0).mean() < 0.012
+
+
+def test_row_outliers_scale_whole_rows():
+    q, k, _ = inputs.draw_fp32(2, 4, 2, 2048, 16, seed=0, outliers="rows")
+    q0, _, _ = inputs.draw_fp32(2, 4, 2, 2048, 16, seed=0)
+    rows = (q != q0).any(-1)
+    assert np.array_equal(q[rows], q0[rows] * 8)
+    assert 0.006 < rows.mean() < 0.014
+
+
+def test_workload_table():
+    w = inputs.WORKLOADS["t16384_d128"]
+    assert (w.B, w.Hq, w.Hkv, w.T, w.D, w.dtype, w.causal) == (1, 32, 8, 16384, 128, "bf16", True)
+    assert abs(w.flops - 2.199e12) / 2.199e12 < 1e-3
+    assert inputs.default_scale(128) == float(np.float32(1 / np.sqrt(128)))
+    assert inputs.WORKLOADS["fp32_t64"].dtype == "fp32"

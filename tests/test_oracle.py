@@ -1,0 +1,105 @@
+"""CPU tests of the fp64 oracle: its pins, planted mistakes, and its argument checks."""
+from __future__ import annotations
+
+import ctypes
+import subprocess
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.oracle import OracleLib, SOURCE
+from tests import oracle_pins
+from tests.oracle_pins import ALL_PINS, rand_inputs
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return oracle.load()
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(lib, pin):
+    pin(lib)
+
+
+# Plausible mistakes, each planted in a copy of the oracle source.  Every one
+# must make at least one pin fail; a mutant that passes them all would mean the
+# pins leave that part of the oracle unchecked.
+MUTANTS = {
+    "interleaved_head_map": ("const int g = h / G;", "const int g = h % Hkv;"),
+    "mask_hides_diagonal": ("causal ? i + 1 : T", "causal ? i : T"),
+    "mask_leaks_next_key": ("causal ? i + 1 : T", "causal ? (i + 2 < T ? i + 2 : T) : T"),
+    "mask_ignored": ("causal ? i + 1 : T", "T"),
+    "scale_dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "scale_squared": ("s[j] = scale * dot;", "s[j] = scale * scale * dot;"),
+    "lse_without_max": ("*lse = m + log(Z);", "*lse = log(Z);"),
+    "lse_log2": ("*lse = m + log(Z);", "*lse = m + log2(Z);"),
+    "unnormalised": ("const double w = p[j] / Z;", "const double w = p[j];"),
+    "scores_use_v": ("dot += widen(q, dtype, qrow + d) * widen(k,",
+                     "dot += widen(q, dtype, qrow + d) * widen(v,"),
+    "exp_sign_flipped": ("p[j] = exp(s[j] - m);", "p[j] = exp(m - s[j]);"),
+    "dropped_last_dim": ("for (int d = 0; d < D; ++d)\n            dot +=",
+                         "for (int d = 0; d < D - 1; ++d)\n            dot +="),
+    "bf16_widen_shift": ("<< 16;", "<< 15;"),
+    "query_row_stride": ("* T + i) * D;", "* T + i) * D + (i > 0);"),
+    "value_from_query_head": ("o[d] += w * widen(v, dtype, kv0 +",
+                              "o[d] += w * widen(v, dtype, (int64_t)0 * kv0 +"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(tmp_path: Path, name):
+    old, new = MUTANTS[name]
+    src = SOURCE.read_text()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new, 1))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", str(mutated),
+                    "-o", str(so), "-lm"], check=True)
+    mutant = OracleLib(so)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, RuntimeError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin rejects the planted mistake {name}"
+
+
+def test_thread_count_does_not_change_bits(lib):
+    q, k, v = rand_inputs(2, 4, 2, 40, 16, "bf16", seed=21)
+    O1, l1 = lib.attn_fwd(q, k, v, True, 0.25, nthreads=1)
+    O8, l8 = lib.attn_fwd(q, k, v, True, 0.25, nthreads=0)
+    assert np.array_equal(O1, O8) and np.array_equal(l1, l8)
+
+
+def test_argument_errors(lib):
+    q, k, v = rand_inputs(1, 4, 2, 8, 4, "fp32", seed=0)
+    c = lib.lib
+    O = np.empty((1, 4, 8, 4))
+    lse = np.empty((1, 4, 8))
+    dp = ctypes.POINTER(ctypes.c_double)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    args = lambda **kw: [kw.get("q", ptr(q)), ptr(k), ptr(v), kw.get("dtype", 0),  # noqa: E731
+                         kw.get("B", 1), kw.get("Hq", 4), kw.get("Hkv", 2), kw.get("T", 8),
+                         kw.get("D", 4), kw.get("causal", 1), 0.5,
+                         O.ctypes.data_as(dp), lse.ctypes.data_as(dp), 1]
+    assert c.tessera_oracle_attn_fwd(*args()) == 0
+    assert c.tessera_oracle_attn_fwd(*args(q=None)) == 1
+    assert c.tessera_oracle_attn_fwd(*args(dtype=5)) == 2
+    assert c.tessera_oracle_attn_fwd(*args(T=0)) == 3
+    assert c.tessera_oracle_attn_fwd(*args(Hq=3)) == 4
+    assert c.tessera_oracle_attn_fwd(*args(causal=2)) == 5
+    with pytest.raises(ValueError):
+        lib.attn_fwd(q.astype(np.float64), k, v, True, 0.5)
+    with pytest.raises(RuntimeError):
+        lib.attn_rows(q, k, v, True, 0.5, np.array([4 * 8], np.int64))
+
+
+def test_pins_module_is_standalone():
+    # the pins must not lean on the HIP package
+    text = Path(oracle_pins.__file__).read_text()
+    assert "attention_flashattention_fwd_amd" not in text
