@@ -1,0 +1,145 @@
+"""Thin ctypes binding over the C ABI in include/tessera_attn.h.
+
+Argument marshalling only: every step of the attention forward pass runs in
+the HIP kernels of libtessera_attn.so.  torch supplies device memory and the
+current stream.  There is no fallback: without the built library, or without
+a GPU, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+import numpy as np
+
+PKG = Path(__file__).resolve().parent
+LIBRARY = PKG / "libtessera_attn.so"
+
+# status codes (enum tessera_attn_status)
+OK = 0
+ERR_NULL = 1
+ERR_SHAPE = 2
+ERR_UNSUPPORTED = 3
+ERR_CAUSAL = 4
+ERR_SCALE = 5
+ERR_ALIGN = 6
+ERR_ALIAS = 7
+ERR_TOO_LARGE = 8
+ERR_LAUNCH = 9
+
+EXPORTS = ("tessera_attn_fwd", "tessera_attn_fwd_f32", "tessera_attn_status_string",
+           "tessera_attn_last_error", "tessera_attn_version")
+
+_lib = None
+
+
+def library_path() -> Path:
+    return LIBRARY
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIBRARY.exists():
+            raise RuntimeError(
+                f"{LIBRARY} is missing: build it with "
+                "`python -m attention_flashattention_fwd_amd.build` (needs ROCm hipcc)")
+        L = ctypes.CDLL(str(LIBRARY))
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        sig = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        L.tessera_attn_fwd.argtypes = sig
+        L.tessera_attn_fwd.restype = i
+        L.tessera_attn_fwd_f32.argtypes = sig
+        L.tessera_attn_fwd_f32.restype = i
+        L.tessera_attn_status_string.argtypes = [i]
+        L.tessera_attn_status_string.restype = ctypes.c_char_p
+        L.tessera_attn_last_error.argtypes = []
+        L.tessera_attn_last_error.restype = ctypes.c_char_p
+        L.tessera_attn_version.argtypes = []
+        L.tessera_attn_version.restype = i
+        _lib = L
+    return _lib
+
+
+def version() -> int:
+    return int(lib().tessera_attn_version())
+
+
+def status_string(code: int) -> str:
+    return lib().tessera_attn_status_string(int(code)).decode()
+
+
+def raw_fwd(dtype: str, q, k, v, out, lse, B, Hq, Hkv, T, D, causal, scale, stream) -> int:
+    """Call the C entry point with integer device addresses; returns the status."""
+    fn = lib().tessera_attn_fwd if dtype == "bf16" else lib().tessera_attn_fwd_f32
+    return int(fn(q, k, v, out, lse, int(B), int(Hq), int(Hkv), int(T), int(D), int(causal),
+                  float(np.float32(scale)), stream))
+
+
+def _check_inputs(q, k, v):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, T, D], got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, Hq, T, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != T or k.shape[3] != D:
+        raise ValueError(f"k, v must be [B, Hkv, T, D] = [{B}, Hkv, {T}, {D}]; "
+                         f"got {tuple(k.shape)} and {tuple(v.shape)}")
+    return B, Hq, k.shape[1], T, D
+
+
+def attn_fwd_into(q, k, v, out, lse, causal: bool = True, scale: float | None = None,
+                  stream=None) -> None:
+    """Write attention of (q, k, v) into preallocated `out` [B,Hq,T,D] (q's
+    dtype) and `lse` [B,Hq,T] float32.  Enqueued on `stream` (default: the
+    current torch stream of q's device); nothing is allocated."""
+    import torch
+
+    B, Hq, Hkv, T, D = _check_inputs(q, k, v)
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, Hq, T) or lse.dtype != torch.float32 or lse.device != q.device \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, T] on q's device")
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    dtype = "bf16" if q.dtype == torch.bfloat16 else "fp32"
+    with torch.cuda.device(q.device):
+        st = raw_fwd(dtype, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                     lse.data_ptr(), B, Hq, Hkv, T, D, int(bool(causal)), scale, handle)
+    if st != OK:
+        msg = status_string(st)
+        if st == ERR_LAUNCH:
+            msg += ": " + lib().tessera_attn_last_error().decode()
+        raise RuntimeError(f"tessera_attn_fwd failed ({st}): {msg}")
+
+
+def attn_fwd(q, k, v, causal: bool = True, scale: float | None = None):
+    """Attention forward.  Returns (out [B,Hq,T,D] in q's dtype, lse [B,Hq,T] float32).
+
+    q [B,Hq,T,D], k/v [B,Hkv,T,D], contiguous, all bfloat16 or all float32,
+    on one GPU.  scale defaults to float32(1/sqrt(D))."""
+    import torch
+
+    B, Hq, Hkv, T, D = _check_inputs(q, k, v)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    attn_fwd_into(q, k, v, out, lse, causal, scale)
+    return out, lse

@@ -1,0 +1,512 @@
+// tessera_attn.hip -- gfx950 (MI355X) kernels and C ABI for the attention
+// forward pass with online softmax, causal masking and grouped-query attention
+// (page "Tessera: a from-scratch distillation and serving stack in one
+// repository", section "The kernel set and its torch fallback").
+//
+// Two kernels:
+//   * attn_fwd_bf16_kernel -- the hot path.  Both contractions (Q K^T and P V)
+//     run on v_mfma_f32_32x32x16_bf16 in a transposed form, S^T = K Q^T and
+//     O^T = V^T P^T, so that every lane owns one query row: the softmax row
+//     statistics live in a lane (plus its partner lane 32 away) instead of
+//     being spread over the wave.  K/V tiles are staged through LDS, double
+//     buffered, and one staged tile serves the query heads of a GQA group.
+//   * attn_fwd_f32_kernel -- fp32 inputs, computed on the vector ALUs in fp32.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "tessera_attn.h"
+
+#define TESSERA_VERSION 10000
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr double kLog2e = 1.442695040888963407;
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel
+// ---------------------------------------------------------------------------
+constexpr int kWaves = 8;                 // waves per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kKeyTile = 64;              // keys per staged K/V tile
+// The running maximum is only raised when a tile's maximum exceeds it by more
+// than this (log2 units).  Any stale maximum gives the same result: it cancels
+// between the numerator and the row sum; it only bounds p by 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
+// LDS chunk swizzles (16-byte chunks of a D-wide bf16 row).  K is read as
+// 16-byte MFMA operands, one key row per lane; V is read with transposing
+// 8-byte reads, eight key rows per quarter-wave.  Each XOR spreads the rows a
+// read touches over distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int key) {
+    if constexpr (D == 128) return key & 15;
+    else if constexpr (D == 64) return (key >> 1) & 7;
+    else return (key >> 2) & 3;
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int key) {
+    if constexpr (D == 128) return (key & 7) << 1;
+    else if constexpr (D == 64) return ((key >> 1) & 1) << 2;
+    else return 0;
+}
+
+struct Bf16Args {
+    const uint16_t *q, *k, *v;
+    uint16_t *o;
+    float *lse;
+    int Hq, Hkv, T, G;
+    int hg;       // heads of one GQA group handled by a workgroup
+    int nqb;      // 32-row query blocks per workgroup (kWaves / hg)
+    int nslots;   // workgroups sharing one (query tile, KV head): G / hg
+    int nbh;      // B * Hkv
+    int nqt;      // query tiles per head
+    int causal;
+    int qmode;    // 0: q as given, 1: q negated (scale < 0), 2: q zeroed (scale == 0)
+    float c;      // |scale| * log2(e)  (1 when scale == 0)
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Work split.  A workgroup owns one query tile of 32*nqb rows for hg query
+// heads of one KV head; wave w takes head (w % hg) and query block (w / hg).
+// Its waves therefore read the same K/V rows, staged once in LDS.  Workgroup
+// ids run over (KV head, slot) fastest so that, with B*Hkv a multiple of the
+// 8 XCDs, every tile of one KV head lands on the same XCD and its L2; causal
+// query tiles are issued longest first.
+template <int D>
+__global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
+    constexpr int kRowBytes = D * 2;
+    constexpr int kCpr = D / 8;                       // 16-byte chunks per row
+    constexpr int kTileBytes = kKeyTile * kRowBytes;
+    constexpr int kChunks = kKeyTile * kCpr;          // chunks per K (or V) tile
+    constexpr int kLoads = (kChunks + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // K0 V0 K1 V1
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int hi = lane >> 5;     // which half of the wave
+    const int col = lane & 31;    // query column of this lane
+
+    const int per_tile = a.nbh * a.nslots;
+    const int qt_rev = blockIdx.x / per_tile;
+    const int rem = blockIdx.x - qt_rev * per_tile;
+    const int qt = a.causal ? (a.nqt - 1 - qt_rev) : qt_rev;
+    const int slot = rem / a.nbh;
+    const int bh = rem - slot * a.nbh;                // b * Hkv + kv head
+    const int b = bh / a.Hkv;
+    const int hkv = bh - b * a.Hkv;
+    const int head = hkv * a.G + slot * a.hg + (w % a.hg);
+    const int rows_wg = 32 * a.nqb;
+    const int q0 = qt * rows_wg;
+    const int qw0 = q0 + 32 * (w / a.hg);
+    const int query = qw0 + col;
+    const int T = a.T;
+    const bool causal = a.causal != 0;
+
+    const int64_t q_row0 = ((int64_t)b * a.Hq + head) * T;
+    const int64_t kv_row0 = (int64_t)bh * T;
+
+    // Q fragment (B operand of S^T = K Q^T): lane holds 8 dims of its query
+    // row per 16-dim step.  Rows past T are clamped; their results are dropped.
+    bf16x8 qf[D / 16];
+    {
+        const uint16_t *src = a.q + (q_row0 + min(query, T - 1)) * D + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 raw = *(const u32x4 *)(src + 16 * ks);
+            if (a.qmode == 1) raw ^= 0x80008000u;
+            else if (a.qmode == 2) raw = 0u;
+            qf[ks] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+
+    const int q_end = min(q0 + rows_wg, T);
+    const int kv_end = causal ? q_end : T;
+    const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
+
+    // K/V staging through registers: global 16-byte loads of tile t+1 are in
+    // flight while tile t is computed, then written to the other LDS buffer.
+    u32x4 kreg[kLoads], vreg[kLoads];
+    auto gload = [&](int j0) {
+#pragma unroll
+        for (int r = 0; r < kLoads; ++r) {
+            const int f = tid + kThreads * r;
+            if (kChunks % kThreads == 0 || f < kChunks) {
+                const int key = f / kCpr, c = f % kCpr;
+                const int64_t row = kv_row0 + min(j0 + key, T - 1);
+                kreg[r] = *(const u32x4 *)(a.k + row * D + 8 * c);
+                vreg[r] = *(const u32x4 *)(a.v + row * D + 8 * c);
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+        char *kb = smem + buf * 2 * kTileBytes;
+        char *vb = kb + kTileBytes;
+#pragma unroll
+        for (int r = 0; r < kLoads; ++r) {
+            const int f = tid + kThreads * r;
+            if (kChunks % kThreads == 0 || f < kChunks) {
+                const int key = f / kCpr, c = f % kCpr;
+                *(u32x4 *)(kb + key * kRowBytes + ((c ^ swz_k<D>(key)) << 4)) = kreg[r];
+                *(u32x4 *)(vb + key * kRowBytes + ((c ^ swz_v<D>(key)) << 4)) = vreg[r];
+            }
+        }
+    };
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    float m_run = -INFINITY;   // running max of scale*log2(e)*s (log2 units)
+    float l_run = 0.f;         // this lane's share of the running row sum
+    const float c = a.c;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int j0 = t * kKeyTile;
+        const bool more = t + 1 < ntiles;
+        if (more) gload(j0 + kKeyTile);
+        const char *kb = smem + (t & 1) * 2 * kTileBytes;
+        const char *vb = kb + kTileBytes;
+
+        // 32-key blocks of this tile: run = some key visible to this wave,
+        // mask = some key hidden from some query of this wave.
+        bool run[2], msk[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int k0 = j0 + 32 * kk;
+            run[kk] = k0 < T && (!causal || k0 <= qw0 + 31);
+            msk[kk] = (k0 + 31 >= T) || (causal && k0 + 31 > qw0);
+        }
+
+        if (run[0] || run[1]) {
+            // S^T = K Q^T: lane holds 16 keys (rows) of its query (column).
+            f32x16 s[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                s[kk] = f32x16{};
+                if (!run[kk]) continue;
+                const int key = 32 * kk + col;
+                const char *krow = kb + key * kRowBytes;
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const bf16x8 kf =
+                        *(const bf16x8 *)(krow + (((2 * ks + hi) ^ swz_k<D>(key)) << 4));
+                    s[kk] = mfma32(kf, qf[ks], s[kk]);
+                }
+                if (msk[kk]) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int kidx = j0 + 32 * kk + 8 * (i >> 2) + 4 * hi + (i & 3);
+                        if (kidx >= T || (causal && kidx > query)) s[kk][i] = -INFINITY;
+                    }
+                }
+            }
+
+            // Online softmax, in log2 units.
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (!run[kk]) continue;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kk][i]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_tile = mx * c;
+            if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+                const float m_new = fmaxf(m_run, m_tile);
+                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+                m_run = m_new;
+            }
+            const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
+
+            // P = 2^(s*c - m) rounded to bf16; the row sum adds the rounded values.
+            u32x4 pu[2][2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (!run[kk]) continue;
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 8 * cc + 2 * e;
+                        f32x2 x;
+                        x[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk][i], c, -m_sub));
+                        x[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk][i + 1], c, -m_sub));
+                        const bf16x2 pb = __builtin_convertvector(x, bf16x2);
+                        l_run = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_run, false);
+                        pu[kk][cc][e] = __builtin_bit_cast(uint32_t, pb);
+                    }
+                }
+            }
+
+            // O^T += V^T P^T.  The 16 keys of one MFMA step are, for lane half
+            // hi, keys {4hi..4hi+3, 8+4hi..8+4hi+3} of the step: exactly the
+            // keys the lane holds in S^T, so P needs no data movement.  V^T is
+            // read from row-major V with two transposing reads.
+            const int grp = lane >> 4, s16 = lane & 15;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const int d = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
+                const int dbyte = (d & 7) * 2;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (!run[kk]) continue;
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) {
+                        const int key1 = 32 * kk + 16 * cc + 4 * hi + (s16 >> 2);
+                        const int key2 = key1 + 8;
+                        const char *p1 = vb + key1 * kRowBytes + (((d >> 3) ^ swz_v<D>(key1)) << 4) + dbyte;
+                        const char *p2 = vb + key2 * kRowBytes + (((d >> 3) ^ swz_v<D>(key2)) << 4) + dbyte;
+                        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p1);
+                        const i16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p2);
+                        const i16x8 vv = __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7);
+                        acc[db] = mfma32(__builtin_bit_cast(bf16x8, vv),
+                                         __builtin_bit_cast(bf16x8, pu[kk][cc]), acc[db]);
+                    }
+                }
+            }
+        }
+
+        if (more) lstore((t + 1) & 1);
+        __syncthreads();
+    }
+
+    // Epilogue: O = acc / l, rounded once to bf16; lse = ln 2 * (m + log2 l).
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (query < T) {
+        const float inv = 1.f / l_tot;
+        uint16_t *dst = a.o + (q_row0 + query) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g4 + e] * inv;
+                const bf16x4 y = __builtin_convertvector(x, bf16x4);
+                *(bf16x4 *)(dst + 32 * db + 8 * g4 + 4 * hi) = y;
+            }
+        }
+        if (hi == 0) a.lse[q_row0 + query] = (m_run + log2f(l_tot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (vector ALUs): 64 query rows per workgroup, four lanes per row,
+// each lane owning D/4 interleaved dims; K/V tiles staged in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kF32Rows = 64;
+constexpr int kF32Keys = 64;
+
+template <int D>
+__global__ void __launch_bounds__(256)
+attn_fwd_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
+                    const float *__restrict__ v, float *__restrict__ out,
+                    float *__restrict__ lse, int Hq, int Hkv, int T, int ntiles, int causal,
+                    float scale) {
+    constexpr int kPer = D / 4;
+    __shared__ __attribute__((aligned(16))) float sk[kF32Keys * D];
+    __shared__ __attribute__((aligned(16))) float sv[kF32Keys * D];
+
+    const int tid = threadIdx.x;
+    const int sub = tid & 3;
+    const int tile = blockIdx.x % ntiles;
+    const int bh = blockIdx.x / ntiles;   // b * Hq + h
+    const int h = bh % Hq;
+    const int b = bh / Hq;
+    const int i = tile * kF32Rows + (tid >> 2);
+    const int64_t kv0 = ((int64_t)b * Hkv + h / (Hq / Hkv)) * T * D;
+    const int64_t qrow = ((int64_t)bh * T + min(i, T - 1)) * D;
+
+    float qr[kPer], acc[kPer];
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+        qr[t] = q[qrow + sub + 4 * t];
+        acc[t] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+
+    const int last_q = min(T, tile * kF32Rows + kF32Rows) - 1;
+    const int kend = causal ? last_q + 1 : T;
+    for (int j0 = 0; j0 < kend; j0 += kF32Keys) {
+        __syncthreads();
+        for (int e = tid; e < kF32Keys * D / 4; e += 256) {
+            const int row = e / (D / 4), c4 = e % (D / 4);
+            float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
+            if (j0 + row < T) {
+                kk = *(const float4 *)(k + kv0 + (int64_t)(j0 + row) * D + 4 * c4);
+                vv = *(const float4 *)(v + kv0 + (int64_t)(j0 + row) * D + 4 * c4);
+            }
+            *(float4 *)(sk + row * D + 4 * c4) = kk;
+            *(float4 *)(sv + row * D + 4 * c4) = vv;
+        }
+        __syncthreads();
+        const int jn = min(kF32Keys, kend - j0);
+        for (int jj = 0; jj < jn; ++jj) {
+            float part = 0.f;
+#pragma unroll
+            for (int t = 0; t < kPer; ++t) part += qr[t] * sk[jj * D + sub + 4 * t];
+            part += __shfl_xor(part, 1);
+            part += __shfl_xor(part, 2);
+            if (causal && j0 + jj > i) continue;   // same decision for the row's four lanes
+            const float s = part * scale;
+            const float mn = fmaxf(m, s);
+            const float alpha = expf(m - mn);
+            const float p = expf(s - mn);
+            l = l * alpha + p;
+#pragma unroll
+            for (int t = 0; t < kPer; ++t) acc[t] = acc[t] * alpha + p * sv[jj * D + sub + 4 * t];
+            m = mn;
+        }
+    }
+    if (i < T) {
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) out[qrow + sub + 4 * t] = acc[t] * inv;
+        if (sub == 0) lse[(int64_t)bh * T + i] = m + logf(l);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+thread_local char g_last_error[256] = "";
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int validate(const void *q, const void *k, const void *v, const void *out, const void *lse,
+             int B, int Hq, int Hkv, int T, int D, int causal, float scale, size_t elem) {
+    if (!q || !k || !v || !out || !lse) return TESSERA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Hq % Hkv != 0) return TESSERA_ERR_SHAPE;
+    if (D != 32 && D != 64 && D != 128) return TESSERA_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return TESSERA_ERR_CAUSAL;
+    if (!isfinite(scale)) return TESSERA_ERR_SCALE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return TESSERA_ERR_ALIGN;
+    if ((uintptr_t)lse & 3u) return TESSERA_ERR_ALIGN;
+    const size_t qbytes = (size_t)B * Hq * T * D * elem;
+    const size_t kvbytes = (size_t)B * Hkv * T * D * elem;
+    const size_t lbytes = (size_t)B * Hq * T * sizeof(float);
+    if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kvbytes) ||
+        overlaps(out, qbytes, v, kvbytes) || overlaps(lse, lbytes, q, qbytes) ||
+        overlaps(lse, lbytes, k, kvbytes) || overlaps(lse, lbytes, v, kvbytes) ||
+        overlaps(lse, lbytes, out, qbytes))
+        return TESSERA_ERR_ALIAS;
+    return TESSERA_OK;
+}
+
+int launch_status(void) {
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) return TESSERA_OK;
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    return TESSERA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int tessera_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+                                int B, int Hq, int Hkv, int T, int D, int causal, float scale,
+                                void *stream) {
+    const int st = validate(q, k, v, out, lse, B, Hq, Hkv, T, D, causal, scale, 2);
+    if (st != TESSERA_OK) return st;
+
+    Bf16Args a;
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.o = (uint16_t *)out;
+    a.lse = lse;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.T = T;
+    a.G = Hq / Hkv;
+    a.hg = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
+    a.nqb = kWaves / a.hg;
+    a.nslots = a.G / a.hg;
+    a.nqt = (T + 32 * a.nqb - 1) / (32 * a.nqb);
+    const int64_t grid = (int64_t)a.nqt * B * Hkv * a.nslots;
+    if (grid > 0x7fffffff) return TESSERA_ERR_TOO_LARGE;
+    a.nbh = B * Hkv;
+    a.causal = causal;
+    a.qmode = scale < 0.f ? 1 : (scale == 0.f ? 2 : 0);
+    a.c = scale == 0.f ? 1.0f : (float)(fabs((double)scale) * kLog2e);
+
+    hipStream_t s = (hipStream_t)stream;
+    if (D == 128)
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    else if (D == 64)
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    return launch_status();
+}
+
+extern "C" int tessera_attn_fwd_f32(const float *q, const float *k, const float *v, float *out,
+                                    float *lse, int B, int Hq, int Hkv, int T, int D, int causal,
+                                    float scale, void *stream) {
+    const int st = validate(q, k, v, out, lse, B, Hq, Hkv, T, D, causal, scale, 4);
+    if (st != TESSERA_OK) return st;
+    const int ntiles = (T + kF32Rows - 1) / kF32Rows;
+    const int64_t grid = (int64_t)ntiles * B * Hq;
+    if (grid > 0x7fffffff) return TESSERA_ERR_TOO_LARGE;
+    hipStream_t s = (hipStream_t)stream;
+    if (D == 128)
+        hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, q, k, v,
+                           out, lse, Hq, Hkv, T, ntiles, causal, scale);
+    else if (D == 64)
+        hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, q, k, v,
+                           out, lse, Hq, Hkv, T, ntiles, causal, scale);
+    else
+        hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, dim3((unsigned)grid), dim3(256), 0, s, q, k, v,
+                           out, lse, Hq, Hkv, T, ntiles, causal, scale);
+    return launch_status();
+}
+
+extern "C" const char *tessera_attn_status_string(int status) {
+    switch (status) {
+    case TESSERA_OK: return "ok";
+    case TESSERA_ERR_NULL: return "null pointer argument";
+    case TESSERA_ERR_SHAPE: return "bad shape: B, Hq, Hkv, T must be >= 1 and Hq % Hkv == 0";
+    case TESSERA_ERR_UNSUPPORTED: return "unsupported head dim: D must be 32, 64 or 128";
+    case TESSERA_ERR_CAUSAL: return "causal must be 0 or 1";
+    case TESSERA_ERR_SCALE: return "scale must be finite";
+    case TESSERA_ERR_ALIGN: return "misaligned pointer: q, k, v, out need 16 bytes, lse 4 bytes";
+    case TESSERA_ERR_ALIAS: return "out or lse overlaps an input or each other";
+    case TESSERA_ERR_TOO_LARGE: return "problem too large for one launch grid";
+    case TESSERA_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char *tessera_attn_last_error(void) { return g_last_error; }
+
+extern "C" int tessera_attn_version(void) { return TESSERA_VERSION; }

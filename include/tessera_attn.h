@@ -1,0 +1,91 @@
+/*
+ * tessera_attn.h -- C ABI of the MI355X (gfx950) attention forward library.
+ *
+ * The operation.  The FlashAttention forward pass named on the page "Tessera:
+ * a from-scratch distillation and serving stack in one repository" (section
+ * "The kernel set and its torch fallback", and the README excerpt's
+ * "Kernels" list on topairepos.com): attention with an online softmax,
+ * causal masking and grouped-query attention.  For every batch b, query head
+ * h and query row i, with G = Hq / Hkv and KV head g = h / G:
+ *
+ *     s_ij       = scale * sum_d q[b,h,i,d] * k[b,g,j,d]
+ *     out[b,h,i] = sum_j softmax_j(s_ij) * v[b,g,j,:]
+ *     lse[b,h,i] = ln sum_j exp(s_ij)
+ *
+ * over keys j <= i when causal = 1, over all T keys when causal = 0.  The
+ * online softmax is an exact reformulation; results match the plain
+ * definition up to rounding.
+ *
+ * Layout.  Every tensor is contiguous and row-major with D innermost:
+ *     q   [B, Hq,  T, D]      k, v [B, Hkv, T, D]
+ *     out [B, Hq,  T, D]      (same dtype as q)
+ *     lse [B, Hq,  T]         float32, natural log
+ *
+ * Ownership and streams.  All pointers are device memory owned by the caller
+ * on the device current at the call.  The library allocates nothing, keeps
+ * no pointer after the call, never synchronises and never changes the
+ * current device.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ * default stream) and is complete when that stream reaches it; the caller
+ * keeps every buffer alive until then.  `out` and `lse` must not overlap
+ * q, k, v or each other.
+ *
+ * Errors.  Every argument is checked before anything is enqueued; a failed
+ * check returns its status with no buffer touched and nothing launched.
+ * TESSERA_ERR_LAUNCH means the HIP launch itself failed; the HIP error text
+ * is then available from tessera_attn_last_error() on the calling thread.
+ * No C++ exception crosses this interface and nothing is printed.
+ * The functions hold no state and may be called from several threads.
+ */
+#ifndef TESSERA_ATTN_H
+#define TESSERA_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum tessera_attn_status {
+    TESSERA_OK = 0,
+    TESSERA_ERR_NULL = 1,        /* a pointer argument is NULL */
+    TESSERA_ERR_SHAPE = 2,       /* B, Hq, Hkv or T < 1, or Hq % Hkv != 0 */
+    TESSERA_ERR_UNSUPPORTED = 3, /* D is not 32, 64 or 128 */
+    TESSERA_ERR_CAUSAL = 4,      /* causal is neither 0 nor 1 */
+    TESSERA_ERR_SCALE = 5,       /* scale is NaN or infinite */
+    TESSERA_ERR_ALIGN = 6,       /* q, k, v, out not 16-byte or lse not 4-byte aligned */
+    TESSERA_ERR_ALIAS = 7,       /* out or lse overlaps an input or each other */
+    TESSERA_ERR_TOO_LARGE = 8,   /* the launch grid would exceed 2^31 - 1 workgroups */
+    TESSERA_ERR_LAUNCH = 9       /* the HIP kernel launch failed */
+};
+
+/*
+ * bf16 attention forward.  q, k, v and out hold bfloat16 values (16-bit
+ * patterns); products are accumulated in fp32 and out is rounded once to
+ * bf16 (nearest even).  lse is fp32.  scale is any finite float (0 and
+ * negative values included); it multiplies q.k before the mask and softmax.
+ * Returns a tessera_attn_status.
+ */
+int tessera_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+                     int B, int Hq, int Hkv, int T, int D, int causal, float scale,
+                     void *stream);
+
+/*
+ * fp32 attention forward: the same operation and arguments with float32
+ * q, k, v and out, computed in fp32 throughout.
+ */
+int tessera_attn_fwd_f32(const float *q, const float *k, const float *v, float *out, float *lse,
+                         int B, int Hq, int Hkv, int T, int D, int causal, float scale,
+                         void *stream);
+
+/* Static text naming a status code (never NULL). */
+const char *tessera_attn_status_string(int status);
+
+/* Text of the last TESSERA_ERR_LAUNCH on the calling thread ("" if none). */
+const char *tessera_attn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int tessera_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TESSERA_ATTN_H */

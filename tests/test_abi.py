@@ -1,0 +1,76 @@
+"""CPU tests of the C-ABI library: it loads, exports what the header declares,
+and rejects bad arguments before touching the GPU (no compute call here)."""
+import re
+from pathlib import Path
+
+import pytest
+
+from attention_flashattention_fwd_amd import binding
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "tessera_attn.h"
+
+# fake, well separated, 16-byte aligned device addresses: validation rejects
+# these calls before any HIP call is made, so they are never dereferenced
+Q, K, V, O, L = (1 << 44), (2 << 44), (3 << 44), (4 << 44), (5 << 44)
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tessera_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_loads_and_exports_every_symbol():
+    lib = binding.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert binding.version() == 10000
+
+
+def test_status_strings():
+    for code in range(0, 10):
+        assert binding.status_string(code)
+    assert binding.status_string(123) == "unknown status"
+    assert binding.lib().tessera_attn_last_error() == b""
+
+
+def call(dtype="bf16", q=Q, k=K, v=V, o=O, l=L, B=1, Hq=4, Hkv=2, T=64, D=64, causal=1,
+         scale=0.125):
+    return binding.raw_fwd(dtype, q, k, v, o, l, B, Hq, Hkv, T, D, causal, scale, None)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), binding.ERR_NULL),
+    (dict(l=None), binding.ERR_NULL),
+    (dict(B=0), binding.ERR_SHAPE),
+    (dict(T=0), binding.ERR_SHAPE),
+    (dict(Hkv=0), binding.ERR_SHAPE),
+    (dict(Hq=3), binding.ERR_SHAPE),
+    (dict(D=48), binding.ERR_UNSUPPORTED),
+    (dict(D=256), binding.ERR_UNSUPPORTED),
+    (dict(causal=2), binding.ERR_CAUSAL),
+    (dict(scale=float("nan")), binding.ERR_SCALE),
+    (dict(scale=float("inf")), binding.ERR_SCALE),
+    (dict(q=Q + 8), binding.ERR_ALIGN),
+    (dict(o=O + 2), binding.ERR_ALIGN),
+    (dict(l=L + 2), binding.ERR_ALIGN),
+    (dict(o=Q), binding.ERR_ALIAS),
+    (dict(l=V + 64), binding.ERR_ALIAS),
+    (dict(l=O), binding.ERR_ALIAS),
+    (dict(B=1 << 16, Hq=1 << 15, Hkv=1 << 15, T=1), binding.ERR_TOO_LARGE),
+])
+def test_bad_arguments_are_rejected_before_launch(dtype, kwargs, code):
+    assert call(dtype, **kwargs) == code
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 8, 32, dtype=torch.bfloat16)
+    k = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.attn_fwd(q, k, k)

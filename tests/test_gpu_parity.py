@@ -1,0 +1,179 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bar: bf16 inputs -- max-abs <= 2e-2 and mean-abs <= 2e-3, separately for O and
+lse; fp32 inputs -- max-abs <= 1e-4.  Small shapes compare every element; the
+full-size workloads compare sampled rows (the oracle computes them one by one)
+and check properties that hold at any size on every row.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_flashattention_fwd_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, F32_MAX = 2e-2, 2e-3, 1e-4
+
+
+def say(*msg):
+    print(*msg, flush=True)
+
+
+def run_gpu(q, k, v, causal, scale):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    out, lse = binding.attn_fwd(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check_close(o, l, O_ref, l_ref, dtype, what=""):
+    assert np.isfinite(o).all() and np.isfinite(l).all(), f"non-finite output {what}"
+    eo, el = np.abs(o - O_ref), np.abs(l - l_ref)
+    stats = f"{what} O max {eo.max():.3e} mean {eo.mean():.3e} | lse max {el.max():.3e} mean {el.mean():.3e}"
+    say(stats)
+    if dtype == "bf16":
+        assert eo.max() <= BF16_MAX and eo.mean() <= BF16_MEAN, stats
+        assert el.max() <= BF16_MAX and el.mean() <= BF16_MEAN, stats
+    else:
+        assert eo.max() <= F32_MAX and el.max() <= F32_MAX, stats
+
+
+def full_case(B, Hq, Hkv, T, D, dtype, causal, scale=None, seed=0, outliers=""):
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, T, D, dtype, seed, outliers)
+    scale = inputs.default_scale(D) if scale is None else scale
+    say(f"case B={B} Hq={Hq} Hkv={Hkv} T={T} D={D} {dtype} causal={causal} scale={scale}")
+    o, l = run_gpu(q, k, v, causal, scale)
+    O_ref, l_ref = oracle.attn_fwd(inputs.bits(q), inputs.bits(k), inputs.bits(v), causal, scale)
+    check_close(o, l, O_ref, l_ref, dtype)
+    return q, k, v, o, l
+
+
+def test_the_native_library_is_loaded():
+    lib = binding.lib()
+    assert lib._name == str(binding.library_path())
+    assert binding.library_path().parent.name == "attention_flashattention_fwd_amd"
+
+
+# -- the two small workloads, every element --------------------------------
+def test_fp32_t64_workload():
+    w = inputs.WORKLOADS["fp32_t64"]
+    full_case(w.B, w.Hq, w.Hkv, w.T, w.D, w.dtype, w.causal)
+
+
+def test_tiny_t128_workload():
+    w = inputs.WORKLOADS["tiny_t128"]
+    q, k, v, o, l = full_case(w.B, w.Hq, w.Hkv, w.T, w.D, w.dtype, w.causal)
+    # causal row 0 sees only key 0: p = 1 exactly, so O = V[0] bit for bit
+    G = w.Hq // w.Hkv
+    v0 = np.repeat(v[:, :, 0].float().numpy(), G, axis=1)
+    assert np.array_equal(o[:, :, 0], v0)
+
+
+# -- edge shapes, every element -----------------------------------------------
+EDGE = [
+    # B, Hq, Hkv, T, D, causal
+    (1, 4, 1, 1, 64, True),       # one row
+    (1, 4, 4, 7, 32, True),       # MHA, T below one tile
+    (3, 4, 2, 17, 64, False),
+    (2, 8, 2, 65, 128, True),     # one key past a tile
+    (1, 8, 1, 130, 64, True),     # MQA (G=8: two workgroups per query tile)
+    (2, 6, 2, 200, 32, True),     # G=3: one head per workgroup, eight query blocks
+    (1, 12, 2, 333, 64, False),   # G=6
+    (1, 4, 4, 1000, 128, True),   # MHA, ragged, several tiles
+    (2, 4, 1, 1000, 64, False),
+    (1, 16, 4, 257, 32, True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D,causal", EDGE)
+def test_edge_shapes_bf16(B, Hq, Hkv, T, D, causal):
+    full_case(B, Hq, Hkv, T, D, "bf16", causal, seed=T)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D,causal", [
+    (1, 2, 1, 1, 32, True), (2, 4, 2, 65, 64, True), (1, 4, 4, 130, 128, False),
+    (1, 8, 2, 300, 128, True), (2, 2, 2, 77, 32, False)])
+def test_edge_shapes_fp32(B, Hq, Hkv, T, D, causal):
+    full_case(B, Hq, Hkv, T, D, "fp32", causal, seed=T)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5, 1e-3])
+def test_scale_values(dtype, scale):
+    full_case(2, 8, 2, 150, 64, dtype, True, scale=scale, seed=7)
+
+
+@pytest.mark.parametrize("mode", ["elements", "rows"])
+def test_outliers_small(mode):
+    full_case(2, 8, 2, 600, 64, "bf16", True, seed=3, outliers=mode)
+
+
+def test_side_stream_and_repeatability():
+    q, k, v = (t.cuda() for t in inputs.make_qkv(2, 8, 2, 300, 64, "bf16", seed=11))
+    out1, lse1 = binding.attn_fwd(q, k, v)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out2 = torch.empty_like(q)
+        lse2 = torch.empty_like(lse1)
+        binding.attn_fwd_into(q, k, v, out2, lse2, True, None, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_binding_argument_checks():
+    q = torch.zeros(1, 4, 16, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        binding.attn_fwd(q, k.float(), k)
+    with pytest.raises(ValueError):
+        binding.attn_fwd(q.transpose(1, 2), k, k)
+    with pytest.raises(RuntimeError, match="shape"):
+        binding.attn_fwd(torch.zeros(1, 3, 16, 64, dtype=torch.bfloat16, device="cuda"), k, k)
+    with pytest.raises(RuntimeError, match="head dim"):
+        binding.attn_fwd(q[..., :48].contiguous(), k[..., :48].contiguous(),
+                         k[..., :48].contiguous())
+
+
+# -- the full-size workloads: sampled rows + whole-tensor properties --------
+def sample_rows(B, Hq, T, n_rand, seed):
+    rng = np.random.default_rng(seed)
+    fixed_i = sorted({0, 1, 31, 32, 63, 64, 65, 127, 128, T // 2, T - 65, T - 64, T - 2, T - 1})
+    heads = [(0, 0), (B - 1, Hq - 1), (B // 2, Hq // 2), (0, Hq - 1)]
+    rows = [(b * Hq + h) * T + i for b, h in heads for i in fixed_i if 0 <= i < T]
+    rows += list(rng.integers(0, B * Hq * T, n_rand))
+    return np.unique(np.array(rows, np.int64))
+
+
+@pytest.mark.parametrize("name", ["t2048", "t2048_full", "t4096_outliers",
+                                  "t4096_outlier_rows", "t16384_d128"])
+def test_full_size_workload(name):
+    w = inputs.WORKLOADS[name]
+    say(f"workload {name}: {w.describe()}")
+    q, k, v = inputs.make_workload(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    out, lse = binding.attn_fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    # every row: finite, and (causal) row 0 equals V[0] exactly
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    G = w.Hq // w.Hkv
+    if w.causal:
+        assert torch.equal(out[:, :, 0], vd[:, :, 0].repeat_interleave(G, dim=1))
+        s0 = (qd[:, :, 0].float() * kd[:, :, 0].float().repeat_interleave(G, dim=1)).sum(-1)
+        assert torch.allclose(lse[:, :, 0], s0 * w.scale, atol=1e-3, rtol=0)
+    rows = sample_rows(w.B, w.Hq, w.T, 400, seed=len(name))
+    say(f"oracle on {len(rows)} sampled rows")
+    O_ref, l_ref = oracle.attn_rows(inputs.bits(q), inputs.bits(k), inputs.bits(v), w.causal,
+                                    w.scale, rows)
+    o = out.reshape(-1, w.D)[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+    l = lse.reshape(-1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    check_close(o.astype(np.float64), l.astype(np.float64), O_ref, l_ref, w.dtype, name)
