@@ -86,26 +86,85 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// One K or V tile in LDS: kKeyTile rows of D bf16, 16-byte chunks swizzled.
+template <int D>
+struct LdsTile {
+    __attribute__((aligned(16))) char b[kKeyTile * D * 2];
+};
+
+// Copy key rows [j0, j0 + kKeyTile) of one K or V head into an LDS tile with
+// direct global->LDS 16-byte loads (no registers involved).  Load i of the
+// tile fills LDS chunk slots [64i, 64i + 64) -- slot p of lane p%64 -- so
+// each lane fetches the logical chunk that the swizzle places in its slot.
+// Rows past T are clamped to row T-1: they only ever meet masked scores.
+template <int D, bool IS_V>
+__device__ __forceinline__ void dma_tile(LDS_AS char *dst, const uint16_t *head, int j0, int T,
+                                         int w, int lane) {
+    constexpr int kCpr = D / 8;
+    constexpr int kLoadsPerTile = kKeyTile * kCpr / 64;       // 64-lane loads per tile
+    constexpr int kPerWave = (kLoadsPerTile + kWaves - 1) / kWaves;
+#pragma unroll
+    for (int r = 0; r < kPerWave; ++r) {
+        const int i = w + kWaves * r;
+        if (kLoadsPerTile % kWaves == 0 || i < kLoadsPerTile) {
+            const int p = 64 * i + lane;
+            const int key = p / kCpr;
+            const int c = (p % kCpr) ^ (IS_V ? swz_v<D>(key) : swz_k<D>(key));
+            const uint16_t *src = head + (int64_t)min(j0 + key, T - 1) * D + 8 * c;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (LDS_AS void *)(dst + 64 * 16 * i), 16, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void wait_dma_and_barrier() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS loads have landed
+    __syncthreads();                      // ... and everyone else's
+}
+
+// S^T = K Q^T for one 64-key tile: two 32-key blocks, two independent MFMA
+// chains.  Lane (col, hi) receives keys 8*(i/4) + 4*hi + i%4 (+32 for the
+// second block) of the tile for its query col.
+template <int D>
+__device__ __forceinline__ void scores(const LDS_AS char *kt, const bf16x8 *qf, int col, int hi,
+                                       f32x16 &s0, f32x16 &s1) {
+    constexpr int kRowBytes = D * 2;
+    s0 = f32x16{};
+    s1 = f32x16{};
+    const LDS_AS char *r0 = kt + col * kRowBytes;
+    const LDS_AS char *r1 = kt + (32 + col) * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 k0 = *(const LDS_AS bf16x8 *)(r0 + (((2 * ks + hi) ^ swz_k<D>(col)) << 4));
+        const bf16x8 k1 = *(const LDS_AS bf16x8 *)(r1 + (((2 * ks + hi) ^ swz_k<D>(32 + col)) << 4));
+        s0 = mfma32(k0, qf[ks], s0);
+        s1 = mfma32(k1, qf[ks], s1);
+    }
+}
+
 // Work split.  A workgroup owns one query tile of 32*nqb rows for hg query
 // heads of one KV head; wave w takes head (w % hg) and query block (w / hg).
 // Its waves therefore read the same K/V rows, staged once in LDS.  Workgroup
 // ids run over (KV head, slot) fastest so that, with B*Hkv a multiple of the
 // 8 XCDs, every tile of one KV head lands on the same XCD and its L2; causal
 // query tiles are issued longest first.
+//
+// Pipeline.  Iteration t computes the scores of tile t+1 while it finishes
+// tile t (softmax, then P V), so the MFMAs of the next tile's Q K^T overlap
+// the exponentials of the current one.  LDS holds K(t+1) and V(t) for
+// iteration t while direct loads fill K(t+2) and V(t+1) into the other
+// buffers; the loop is unrolled by two so every buffer is a distinct array.
 template <int D>
 __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     constexpr int kRowBytes = D * 2;
-    constexpr int kCpr = D / 8;                       // 16-byte chunks per row
-    constexpr int kTileBytes = kKeyTile * kRowBytes;
-    constexpr int kChunks = kKeyTile * kCpr;          // chunks per K (or V) tile
-    constexpr int kLoads = (kChunks + kThreads - 1) / kThreads;
-    __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // K0 V0 K1 V1
+    __shared__ LdsTile<D> K0, K1, V0, V1;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int hi = lane >> 5;     // which half of the wave
     const int col = lane & 31;    // query column of this lane
+    const int grp = lane >> 4, s16 = lane & 15;
 
     const int per_tile = a.nbh * a.nslots;
     const int qt_rev = blockIdx.x / per_tile;
@@ -124,54 +183,31 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     const bool causal = a.causal != 0;
 
     const int64_t q_row0 = ((int64_t)b * a.Hq + head) * T;
-    const int64_t kv_row0 = (int64_t)bh * T;
+    const uint16_t *khead = a.k + (int64_t)bh * T * D;
+    const uint16_t *vhead = a.v + (int64_t)bh * T * D;
+
+    const int q_end = min(q0 + rows_wg, T);
+    const int kv_end = causal ? q_end : T;
+    const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
+
+    // Prologue loads: K(0), V(0), K(1).
+    dma_tile<D, false>((LDS_AS char *)K0.b, khead, 0, T, w, lane);
+    dma_tile<D, true>((LDS_AS char *)V0.b, vhead, 0, T, w, lane);
+    dma_tile<D, false>((LDS_AS char *)K1.b, khead, kKeyTile, T, w, lane);
 
     // Q fragment (B operand of S^T = K Q^T): lane holds 8 dims of its query
     // row per 16-dim step.  Rows past T are clamped; their results are dropped.
     bf16x8 qf[D / 16];
     {
         const uint16_t *src = a.q + (q_row0 + min(query, T - 1)) * D + 8 * hi;
+        const uint32_t flip = a.qmode == 1 ? 0x80008000u : 0u;
+        const uint32_t keep = a.qmode == 2 ? 0u : 0xffffffffu;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-            u32x4 raw = *(const u32x4 *)(src + 16 * ks);
-            if (a.qmode == 1) raw ^= 0x80008000u;
-            else if (a.qmode == 2) raw = 0u;
-            qf[ks] = __builtin_bit_cast(bf16x8, raw);
+            const u32x4 raw = *(const u32x4 *)(src + 16 * ks);
+            qf[ks] = __builtin_bit_cast(bf16x8, (raw ^ flip) & keep);
         }
     }
-
-    const int q_end = min(q0 + rows_wg, T);
-    const int kv_end = causal ? q_end : T;
-    const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
-
-    // K/V staging through registers: global 16-byte loads of tile t+1 are in
-    // flight while tile t is computed, then written to the other LDS buffer.
-    u32x4 kreg[kLoads], vreg[kLoads];
-    auto gload = [&](int j0) {
-#pragma unroll
-        for (int r = 0; r < kLoads; ++r) {
-            const int f = tid + kThreads * r;
-            if (kChunks % kThreads == 0 || f < kChunks) {
-                const int key = f / kCpr, c = f % kCpr;
-                const int64_t row = kv_row0 + min(j0 + key, T - 1);
-                kreg[r] = *(const u32x4 *)(a.k + row * D + 8 * c);
-                vreg[r] = *(const u32x4 *)(a.v + row * D + 8 * c);
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
-        char *kb = smem + buf * 2 * kTileBytes;
-        char *vb = kb + kTileBytes;
-#pragma unroll
-        for (int r = 0; r < kLoads; ++r) {
-            const int f = tid + kThreads * r;
-            if (kChunks % kThreads == 0 || f < kChunks) {
-                const int key = f / kCpr, c = f % kCpr;
-                *(u32x4 *)(kb + key * kRowBytes + ((c ^ swz_k<D>(key)) << 4)) = kreg[r];
-                *(u32x4 *)(vb + key * kRowBytes + ((c ^ swz_v<D>(key)) << 4)) = vreg[r];
-            }
-        }
-    };
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -181,121 +217,104 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     const float c = a.c;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    wait_dma_and_barrier();
+    f32x16 s0, s1;            // scores of the tile being finished
+    scores<D>((const LDS_AS char *)K0.b, qf, col, hi, s0, s1);
+    __syncthreads();          // K0 is refilled by the first iteration
 
-    for (int t = 0; t < ntiles; ++t) {
+    // One pipeline step: finish tile t (scores in s0/s1) reading V(t) from vt,
+    // compute the scores of tile t+1 from kn, and refill kw <- K(t+2),
+    // vw <- V(t+1).
+    auto step = [&](int t, const LDS_AS char *kn, const LDS_AS char *vt, LDS_AS char *kw,
+                    LDS_AS char *vw) {
         const int j0 = t * kKeyTile;
-        const bool more = t + 1 < ntiles;
-        if (more) gload(j0 + kKeyTile);
-        const char *kb = smem + (t & 1) * 2 * kTileBytes;
-        const char *vb = kb + kTileBytes;
-
-        // 32-key blocks of this tile: run = some key visible to this wave,
-        // mask = some key hidden from some query of this wave.
-        bool run[2], msk[2];
+        // Mask keys hidden from a query (diagonal tile) or past T (ragged tile).
+        if ((j0 + kKeyTile > T) || (causal && j0 + kKeyTile - 1 > qw0)) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int k0 = j0 + 32 * kk;
-            run[kk] = k0 < T && (!causal || k0 <= qw0 + 31);
-            msk[kk] = (k0 + 31 >= T) || (causal && k0 + 31 > qw0);
+            for (int i = 0; i < 16; ++i) {
+                const int kidx = j0 + 8 * (i >> 2) + 4 * hi + (i & 3);
+                if (kidx >= T || (causal && kidx > query)) s0[i] = -INFINITY;
+                if (kidx + 32 >= T || (causal && kidx + 32 > query)) s1[i] = -INFINITY;
+            }
+        }
+        // Online softmax, in log2 units; the running max only moves when a
+        // tile beats it by more than kRescaleSlack.
+        float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s0[1], s1[1]);
+#pragma unroll
+        for (int i = 2; i < 16; i += 2) {
+            ma = fmaxf(fmaxf(ma, s0[i]), s1[i]);
+            mb = fmaxf(fmaxf(mb, s0[i + 1]), s1[i + 1]);
+        }
+        float mx = fmaxf(ma, mb);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_tile = mx * c;
+        if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+            const float m_new = fmaxf(m_run, m_tile);
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
+
+        dma_tile<D, false>(kw, khead, j0 + 2 * kKeyTile, T, w, lane);
+        dma_tile<D, true>(vw, vhead, j0 + kKeyTile, T, w, lane);
+
+        // Scores of the next tile (its MFMAs overlap the exponentials below).
+        f32x16 n0, n1;
+        scores<D>(kn, qf, col, hi, n0, n1);
+
+        // P = 2^(s*c - m) rounded to bf16; the row sum adds the rounded values.
+        u32x4 pu[4];   // 16-key steps: keys 0-15, 16-31 (block 0), 32-47, 48-63 (block 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            f32x2 x0, x1;
+            x0[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * e], c, -m_sub));
+            x0[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * e + 1], c, -m_sub));
+            x1[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * e], c, -m_sub));
+            x1[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * e + 1], c, -m_sub));
+            const bf16x2 p0 = __builtin_convertvector(x0, bf16x2);
+            const bf16x2 p1 = __builtin_convertvector(x1, bf16x2);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, l_run, false);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, l_run, false);
+            pu[e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p0);
+            pu[2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
         }
 
-        if (run[0] || run[1]) {
-            // S^T = K Q^T: lane holds 16 keys (rows) of its query (column).
-            f32x16 s[2];
+        // O^T += V^T P^T.  The 16 keys of one MFMA step are, for lane half
+        // hi, keys {4hi..4hi+3, 8+4hi..8+4hi+3} of the step: exactly the
+        // keys the lane holds in S^T, so P needs no data movement.  V^T is
+        // read from row-major V with two transposing reads; the D/32
+        // accumulators make independent MFMA chains.
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                s[kk] = f32x16{};
-                if (!run[kk]) continue;
-                const int key = 32 * kk + col;
-                const char *krow = kb + key * kRowBytes;
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const bf16x8 kf =
-                        *(const bf16x8 *)(krow + (((2 * ks + hi) ^ swz_k<D>(key)) << 4));
-                    s[kk] = mfma32(kf, qf[ks], s[kk]);
-                }
-                if (msk[kk]) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int kidx = j0 + 32 * kk + 8 * (i >> 2) + 4 * hi + (i & 3);
-                        if (kidx >= T || (causal && kidx > query)) s[kk][i] = -INFINITY;
-                    }
-                }
-            }
-
-            // Online softmax, in log2 units.
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (!run[kk]) continue;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kk][i]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_tile = mx * c;
-            if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
-                const float m_new = fmaxf(m_run, m_tile);
-                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-                m_run = m_new;
-            }
-            const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
-
-            // P = 2^(s*c - m) rounded to bf16; the row sum adds the rounded values.
-            u32x4 pu[2][2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (!run[kk]) continue;
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 8 * cc + 2 * e;
-                        f32x2 x;
-                        x[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk][i], c, -m_sub));
-                        x[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk][i + 1], c, -m_sub));
-                        const bf16x2 pb = __builtin_convertvector(x, bf16x2);
-                        l_run = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_run, false);
-                        pu[kk][cc][e] = __builtin_bit_cast(uint32_t, pb);
-                    }
-                }
-            }
-
-            // O^T += V^T P^T.  The 16 keys of one MFMA step are, for lane half
-            // hi, keys {4hi..4hi+3, 8+4hi..8+4hi+3} of the step: exactly the
-            // keys the lane holds in S^T, so P needs no data movement.  V^T is
-            // read from row-major V with two transposing reads.
-            const int grp = lane >> 4, s16 = lane & 15;
+        for (int st = 0; st < 4; ++st) {
+            const int r1 = 16 * st + 4 * hi + (s16 >> 2);
+            const int r2 = r1 + 8;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
                 const int d = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
                 const int dbyte = (d & 7) * 2;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (!run[kk]) continue;
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) {
-                        const int key1 = 32 * kk + 16 * cc + 4 * hi + (s16 >> 2);
-                        const int key2 = key1 + 8;
-                        const char *p1 = vb + key1 * kRowBytes + (((d >> 3) ^ swz_v<D>(key1)) << 4) + dbyte;
-                        const char *p2 = vb + key2 * kRowBytes + (((d >> 3) ^ swz_v<D>(key2)) << 4) + dbyte;
-                        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p1);
-                        const i16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p2);
-                        const i16x8 vv = __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7);
-                        acc[db] = mfma32(__builtin_bit_cast(bf16x8, vv),
-                                         __builtin_bit_cast(bf16x8, pu[kk][cc]), acc[db]);
-                    }
-                }
+                const LDS_AS char *p1 = vt + r1 * kRowBytes + (((d >> 3) ^ swz_v<D>(r1)) << 4) + dbyte;
+                const LDS_AS char *p2 = vt + r2 * kRowBytes + (((d >> 3) ^ swz_v<D>(r2)) << 4) + dbyte;
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p1);
+                const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p2);
+                const i16x8 vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[db] = mfma32(__builtin_bit_cast(bf16x8, vv), __builtin_bit_cast(bf16x8, pu[st]),
+                                 acc[db]);
             }
         }
+        s0 = n0;
+        s1 = n1;
+        wait_dma_and_barrier();
+    };
 
-        if (more) lstore((t + 1) & 1);
-        __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, (const LDS_AS char *)K1.b, (const LDS_AS char *)V0.b, (LDS_AS char *)K0.b,
+             (LDS_AS char *)V1.b);
+        if (t + 1 < ntiles)
+            step(t + 1, (const LDS_AS char *)K0.b, (const LDS_AS char *)V1.b, (LDS_AS char *)K1.b,
+                 (LDS_AS char *)V0.b);
     }
 
     // Epilogue: O = acc / l, rounded once to bf16; lse = ln 2 * (m + log2 l).
