@@ -18,7 +18,7 @@ LIBRARY = PKG / "libtessera_attn.so"
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-function",
     # no NaN handling in max/min: inputs are finite by contract, and masked
     # scores are -inf, never NaN

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <utility>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -62,7 +63,7 @@ __device__ __forceinline__ int swz_k(int key) {
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int key) {
-    if constexpr (D == 128) return (key & 7) << 1;
+    if constexpr (D == 128) return ((key & 3) << 2) | (((key >> 2) & 1) << 1);
     else if constexpr (D == 64) return ((key >> 1) & 1) << 2;
     else return 0;
 }
@@ -86,60 +87,190 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// One 16-byte global->LDS load per lane: lane l's 16 bytes, read from
+// base + voff (base uniform, voff per lane), land at LDS byte address
+// lds + 16*l.  Written as inline assembly so that the compiler does not track
+// these LDS writes itself: the kernel orders them explicitly (vmcnt wait plus
+// barrier before any read of the buffer), and the compiler's own tracking
+// would otherwise stall reads of other buffers while a load is in flight.
+// The s_nop covers the M0-write hazard before the load.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // One K or V tile in LDS: kKeyTile rows of D bf16, 16-byte chunks swizzled.
 template <int D>
 struct LdsTile {
     __attribute__((aligned(16))) char b[kKeyTile * D * 2];
 };
 
-// Copy key rows [j0, j0 + kKeyTile) of one K or V head into an LDS tile with
-// direct global->LDS 16-byte loads (no registers involved).  Load i of the
-// tile fills LDS chunk slots [64i, 64i + 64) -- slot p of lane p%64 -- so
-// each lane fetches the logical chunk that the swizzle places in its slot.
-// Rows past T are clamped to row T-1: they only ever meet masked scores.
-template <int D, bool IS_V>
-__device__ __forceinline__ void dma_tile(LDS_AS char *dst, const uint16_t *head, int j0, int T,
-                                         int w, int lane) {
-    constexpr int kCpr = D / 8;
-    constexpr int kLoadsPerTile = kKeyTile * kCpr / 64;       // 64-lane loads per tile
-    constexpr int kPerWave = (kLoadsPerTile + kWaves - 1) / kWaves;
+// The loads that copy key rows [j0, j0 + kKeyTile) of one K or V head into an
+// LDS tile, split over NW waves (this is wave wi of them).  Load i of the tile
+// fills LDS chunk slots [64i, 64i + 64) -- slot p by lane p%64 -- so each lane
+// fetches the logical chunk that the swizzle places in its slot.  The per-lane
+// byte offsets within a tile are fixed; only the tile's base row moves.  Rows
+// past T (last, ragged tile) are clamped to row T-1: they only ever meet
+// masked scores.
+template <int D, bool IS_V, int NW>
+struct TileLoader {
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kCpr = D / 8;
+    static constexpr int kLoadsPerTile = kKeyTile * kCpr / 64;    // 64-lane loads per tile
+    static constexpr int kPerWave = (kLoadsPerTile + NW - 1) / NW;
+    uint32_t off[kPerWave];     // key * row bytes + swizzled chunk * 16
+    int wi;
+
+    __device__ __forceinline__ TileLoader(int wi_, int lane) : wi(wi_) {
 #pragma unroll
-    for (int r = 0; r < kPerWave; ++r) {
-        const int i = w + kWaves * r;
-        if (kLoadsPerTile % kWaves == 0 || i < kLoadsPerTile) {
-            const int p = 64 * i + lane;
+        for (int r = 0; r < kPerWave; ++r) {
+            const int p = 64 * (wi + NW * r) + lane;
             const int key = p / kCpr;
             const int c = (p % kCpr) ^ (IS_V ? swz_v<D>(key) : swz_k<D>(key));
-            const uint16_t *src = head + (int64_t)min(j0 + key, T - 1) * D + 8 * c;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                             (LDS_AS void *)(dst + 64 * 16 * i), 16, 0, 0);
+            off[r] = key * kRowBytes + c * 16;
         }
     }
-}
+    __device__ __forceinline__ bool active(int r) const {
+        return kLoadsPerTile % NW == 0 || wi + NW * r < kLoadsPerTile;
+    }
+    __device__ __forceinline__ void load(LDS_AS char *dst, const uint16_t *head, int j0,
+                                         int T) const {
+        const char *base = (const char *)(head + (int64_t)j0 * D);
+        const uint32_t lds = (uint32_t)(uintptr_t)dst;
+        if (j0 + kKeyTile <= T) {
+#pragma unroll
+            for (int r = 0; r < kPerWave; ++r)
+                if (active(r)) dma16(base, off[r], lds + 1024 * (wi + NW * r));
+        } else {
+            const int last = T - 1 - j0;   // last valid row of this tile
+#pragma unroll
+            for (int r = 0; r < kPerWave; ++r) {
+                if (!active(r)) continue;
+                const int key = (int)(off[r] / kRowBytes);
+                const uint32_t o = (uint32_t)(min(key, last) - key) * kRowBytes + off[r];
+                dma16(base, o, lds + 1024 * (wi + NW * r));
+            }
+        }
+    }
+};
 
 __device__ __forceinline__ void wait_dma_and_barrier() {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS loads have landed
     __syncthreads();                      // ... and everyone else's
 }
 
-// S^T = K Q^T for one 64-key tile: two 32-key blocks, two independent MFMA
-// chains.  Lane (col, hi) receives keys 8*(i/4) + 4*hi + i%4 (+32 for the
-// second block) of the tile for its query col.
+// Per-lane LDS byte offsets of the MFMA operands inside a K or V tile.
+//  * K (A operand of S^T = K Q^T): lane (col, hi) reads 16 bytes of key row col
+//    (and col + 32 for the second 32-key block, a fixed +32 rows), dims
+//    16*ks + 8*hi .. +7, for ks = 0 .. D/16-1.
+//  * V (A operand of O^T = V^T P^T): ds_read_b64_tr_b16 hands lane j of a
+//    16-lane group element j%4 of the 8-byte pieces read by lanes 4r + j/4,
+//    r = 0..3.  For step st and dim block db, lane (grp, s16) reads key row
+//    16*st + 4*hi + s16/4 (and +8 rows), dims 32*db + 16*(grp&1) + 4*(s16&3)
+//    .. +3; after the transpose it holds 8 keys of one dim.  The keys come in
+//    the same order as the lane's rows of S^T, so P needs no data movement.
+//    The st and +8-row parts are fixed offsets; only db needs a register.
 template <int D>
-__device__ __forceinline__ void scores(const LDS_AS char *kt, const bf16x8 *qf, int col, int hi,
-                                       f32x16 &s0, f32x16 &s1) {
-    constexpr int kRowBytes = D * 2;
-    s0 = f32x16{};
-    s1 = f32x16{};
-    const LDS_AS char *r0 = kt + col * kRowBytes;
-    const LDS_AS char *r1 = kt + (32 + col) * kRowBytes;
+struct LaneOffsets {
+    int k[D / 16];
+    int v[D / 32];
+    __device__ __forceinline__ LaneOffsets(int lane) {
+        constexpr int kRowBytes = D * 2;
+        const int col = lane & 31, hi = lane >> 5, grp = lane >> 4, s16 = lane & 15;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 k0 = *(const LDS_AS bf16x8 *)(r0 + (((2 * ks + hi) ^ swz_k<D>(col)) << 4));
-        const bf16x8 k1 = *(const LDS_AS bf16x8 *)(r1 + (((2 * ks + hi) ^ swz_k<D>(32 + col)) << 4));
-        s0 = mfma32(k0, qf[ks], s0);
-        s1 = mfma32(k1, qf[ks], s1);
+        for (int ks = 0; ks < D / 16; ++ks)
+            k[ks] = col * kRowBytes + (((2 * ks + hi) ^ swz_k<D>(col)) << 4);
+        const int r = 4 * hi + (s16 >> 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int d = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
+            v[db] = r * kRowBytes + (((d >> 3) ^ swz_v<D>(r)) << 4) + (d & 7) * 2;
+        }
     }
+};
+
+// The MFMA phase of one tile: S^T(t) = K(t) Q^T (two 32-key blocks, chains
+// s0 and s1) and O^T += V(t-1)^T P(t-1)^T (D/32 chains acc[db]), as one
+// software pipeline.  The D/8 score MFMAs and D/8 P V MFMAs alternate, and the
+// LDS operands are read kPrefetch MFMAs ahead.  MODE: 0 both, 1 scores only
+// (first tile), 2 P V only (after the last tile).
+constexpr int kPrefetch = 4;
+
+// LDS reads feeding op i of an MFMA phase: one 16-byte read for a score MFMA,
+// two transposing 8-byte reads for a P V MFMA.
+constexpr int phase_reads(int mode, int i) {
+    return (mode == 1 || (mode == 0 && (i & 1) == 0)) ? 1 : 2;
+}
+
+// Scheduling groups for the MFMA phase: the reads of the first kPrefetch ops,
+// then for every op its MFMA followed by the reads of the op kPrefetch later.
+// This pins the prefetch distance that the plain schedule would shrink.
+template <int MODE, int I, int N>
+__device__ __forceinline__ void schedule_mfma_phase() {
+    if constexpr (I == 0) {
+        constexpr int pre = N < kPrefetch ? N : kPrefetch;
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            (__builtin_amdgcn_sched_group_barrier(0x100, phase_reads(MODE, J), 0), ...);
+        }(std::make_integer_sequence<int, pre>{});
+    }
+    if constexpr (I < N) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (I + kPrefetch < N)
+            __builtin_amdgcn_sched_group_barrier(0x100, phase_reads(MODE, I + kPrefetch), 0);
+        schedule_mfma_phase<MODE, I + 1, N>();
+    }
+}
+
+template <int D, int MODE>
+__device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS char *vt,
+                                           const LaneOffsets<D> &off, const bf16x8 *qf,
+                                           const u32x4 *pu, f32x16 &s0, f32x16 &s1, f32x16 *acc) {
+    constexpr int kRowBytes = D * 2;
+    constexpr int kHalf = D / 8;                         // MFMAs of each kind
+    constexpr int kN = MODE == 0 ? 2 * kHalf : kHalf;    // MFMAs in this phase
+    // op i -> (is_score, index j within its kind)
+    auto is_score = [](int i) { return MODE == 1 || (MODE == 0 && (i & 1) == 0); };
+    auto index = [](int i) { return MODE == 0 ? (i >> 1) : i; };
+    auto load = [&](int i) __attribute__((always_inline)) -> u32x4 {
+        const int j = index(i);
+        if (is_score(i)) {
+            const int ks = j >> 1, kb = j & 1;
+            return *(const LDS_AS u32x4 *)(kt + off.k[ks] + kb * 32 * kRowBytes);
+        }
+        const int st = j / (D / 32), db = j % (D / 32);
+        const LDS_AS char *p = vt + off.v[db] + st * 16 * kRowBytes;
+        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p);
+        const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(p + 8 * kRowBytes));
+        return __builtin_bit_cast(u32x4, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    if (MODE != 2) {
+        s0 = f32x16{};
+        s1 = f32x16{};
+    }
+    u32x4 ring[kPrefetch];
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) ring[i] = load(i);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+        const u32x4 cur = ring[i % kPrefetch];
+        if (i + kPrefetch < kN) ring[i % kPrefetch] = load(i + kPrefetch);
+        const int j = index(i);
+        if (is_score(i)) {
+            const int ks = j >> 1;
+            if ((j & 1) == 0) s0 = mfma32(__builtin_bit_cast(bf16x8, cur), qf[ks], s0);
+            else s1 = mfma32(__builtin_bit_cast(bf16x8, cur), qf[ks], s1);
+        } else {
+            const int st = j / (D / 32), db = j % (D / 32);
+            acc[db] = mfma32(__builtin_bit_cast(bf16x8, cur), __builtin_bit_cast(bf16x8, pu[st]),
+                             acc[db]);
+        }
+    }
+    schedule_mfma_phase<MODE, 0, kN>();
 }
 
 // Work split.  A workgroup owns one query tile of 32*nqb rows for hg query
@@ -149,22 +280,26 @@ __device__ __forceinline__ void scores(const LDS_AS char *kt, const bf16x8 *qf, 
 // 8 XCDs, every tile of one KV head lands on the same XCD and its L2; causal
 // query tiles are issued longest first.
 //
-// Pipeline.  Iteration t computes the scores of tile t+1 while it finishes
-// tile t (softmax, then P V), so the MFMAs of the next tile's Q K^T overlap
-// the exponentials of the current one.  LDS holds K(t+1) and V(t) for
-// iteration t while direct loads fill K(t+2) and V(t+1) into the other
-// buffers; the loop is unrolled by two so every buffer is a distinct array.
+// Ping-pong.  Each tile is two phases per wave: an MFMA phase (S(t) = K(t)
+// Q^T and acc += V(t-1)^T P(t-1)^T) and a vector phase (mask, online softmax,
+// P(t) = 2^(S c - m) in bf16), separated by barriers.  Waves 0-3 and 4-7 (one
+// of each per SIMD) run the same code one phase apart -- waves 4-7 pass one
+// extra barrier first -- so in every phase one wave of a SIMD feeds the matrix
+// cores while the other works the vector ALUs.  K(t) and V(t-1) stay in LDS
+// for phases 2t and 2t+1; the lagging waves stream K(t+1) and V(t) in with
+// direct global->LDS loads during phase 2t and wait for them at the end of
+// phase 2t+1.  The loop is unrolled by two so every LDS buffer is a distinct
+// array.
 template <int D>
 __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
-    constexpr int kRowBytes = D * 2;
     __shared__ LdsTile<D> K0, K1, V0, V1;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const bool lag = w >= 4;      // the half that runs one phase behind
     const int hi = lane >> 5;     // which half of the wave
     const int col = lane & 31;    // query column of this lane
-    const int grp = lane >> 4, s16 = lane & 15;
 
     const int per_tile = a.nbh * a.nslots;
     const int qt_rev = blockIdx.x / per_tile;
@@ -190,10 +325,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     const int kv_end = causal ? q_end : T;
     const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
 
-    // Prologue loads: K(0), V(0), K(1).
-    dma_tile<D, false>((LDS_AS char *)K0.b, khead, 0, T, w, lane);
-    dma_tile<D, true>((LDS_AS char *)V0.b, vhead, 0, T, w, lane);
-    dma_tile<D, false>((LDS_AS char *)K1.b, khead, kKeyTile, T, w, lane);
+    TileLoader<D, false, kWaves>(w, lane).load((LDS_AS char *)K0.b, khead, 0, T);
 
     // Q fragment (B operand of S^T = K Q^T): lane holds 8 dims of its query
     // row per 16-dim step.  Rows past T are clamped; their results are dropped.
@@ -216,25 +348,28 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     float l_run = 0.f;         // this lane's share of the running row sum
     const float c = a.c;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    f32x16 s0 = f32x16{}, s1 = f32x16{};   // scores of the tile in flight
+    u32x4 pu[4];                           // its probabilities, bf16, per 16-key step
 
     wait_dma_and_barrier();
-    f32x16 s0, s1;            // scores of the tile being finished
-    scores<D>((const LDS_AS char *)K0.b, qf, col, hi, s0, s1);
-    __syncthreads();          // K0 is refilled by the first iteration
 
-    // One pipeline step: finish tile t (scores in s0/s1) reading V(t) from vt,
-    // compute the scores of tile t+1 from kn, and refill kw <- K(t+2),
-    // vw <- V(t+1).
-    auto step = [&](int t, const LDS_AS char *kn, const LDS_AS char *vt, LDS_AS char *kw,
-                    LDS_AS char *vw) {
+    const LaneOffsets<D> off(lane);
+    // Loaders of the lagging waves (they issue every K/V load after the first).
+    const TileLoader<D, false, 4> kload(w & 3, lane);
+    const TileLoader<D, true, 4> vload(w & 3, lane);
+    // Vector phase of tile t: mask, online softmax, P(t).
+    auto softmax_phase = [&](int t) __attribute__((always_inline)) {
         const int j0 = t * kKeyTile;
         // Mask keys hidden from a query (diagonal tile) or past T (ragged tile).
         if ((j0 + kKeyTile > T) || (causal && j0 + kKeyTile - 1 > qw0)) {
+            // Row i of this lane is key j0 + 4*hi + 8*(i/4) + i%4 (+32 in s1);
+            // it is visible iff that key <= last, the last key this query sees.
+            const int last = (causal ? min(query, T - 1) : T - 1) - j0 - 4 * hi;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int kidx = j0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-                if (kidx >= T || (causal && kidx > query)) s0[i] = -INFINITY;
-                if (kidx + 32 >= T || (causal && kidx + 32 > query)) s1[i] = -INFINITY;
+                const int r = 8 * (i >> 2) + (i & 3);
+                if (r > last) s0[i] = -INFINITY;
+                if (r + 32 > last) s1[i] = -INFINITY;
             }
         }
         // Online softmax, in log2 units; the running max only moves when a
@@ -257,16 +392,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
             m_run = m_new;
         }
         const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
-
-        dma_tile<D, false>(kw, khead, j0 + 2 * kKeyTile, T, w, lane);
-        dma_tile<D, true>(vw, vhead, j0 + kKeyTile, T, w, lane);
-
-        // Scores of the next tile (its MFMAs overlap the exponentials below).
-        f32x16 n0, n1;
-        scores<D>(kn, qf, col, hi, n0, n1);
-
         // P = 2^(s*c - m) rounded to bf16; the row sum adds the rounded values.
-        u32x4 pu[4];   // 16-key steps: keys 0-15, 16-31 (block 0), 32-47, 48-63 (block 1)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             f32x2 x0, x1;
@@ -281,41 +407,55 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
             pu[e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p0);
             pu[2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
         }
-
-        // O^T += V^T P^T.  The 16 keys of one MFMA step are, for lane half
-        // hi, keys {4hi..4hi+3, 8+4hi..8+4hi+3} of the step: exactly the
-        // keys the lane holds in S^T, so P needs no data movement.  V^T is
-        // read from row-major V with two transposing reads; the D/32
-        // accumulators make independent MFMA chains.
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int r1 = 16 * st + 4 * hi + (s16 >> 2);
-            const int r2 = r1 + 8;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const int d = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
-                const int dbyte = (d & 7) * 2;
-                const LDS_AS char *p1 = vt + r1 * kRowBytes + (((d >> 3) ^ swz_v<D>(r1)) << 4) + dbyte;
-                const LDS_AS char *p2 = vt + r2 * kRowBytes + (((d >> 3) ^ swz_v<D>(r2)) << 4) + dbyte;
-                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p1);
-                const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p2);
-                const i16x8 vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[db] = mfma32(__builtin_bit_cast(bf16x8, vv), __builtin_bit_cast(bf16x8, pu[st]),
-                                 acc[db]);
-            }
+    };
+    // Iteration t of every wave: the MFMA phase of tile t (S(t) from kc, and
+    // P(t-1) V(t-1) from vp), a barrier, the vector phase of tile t, a barrier.
+    // The lagging waves also issue the loads of K(t+2) into kw and V(t+1) into
+    // vw during their vector phase and wait for them at the end of their next
+    // MFMA phase; by then both buffers' previous tiles have been read.
+    auto finish = [&](int t, LDS_AS char *kw, LDS_AS char *vw) __attribute__((always_inline)) {
+        if (lag) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): its loads have landed
+        __syncthreads();
+        softmax_phase(t);
+        if (lag) {
+            if (t + 2 < ntiles) kload.load(kw, khead, (t + 2) * kKeyTile, T);
+            if (t + 1 < ntiles) vload.load(vw, vhead, (t + 1) * kKeyTile, T);
         }
-        s0 = n0;
-        s1 = n1;
-        wait_dma_and_barrier();
+        __syncthreads();
+    };
+    auto iteration = [&](int t, const LDS_AS char *kc, const LDS_AS char *vp, LDS_AS char *kw,
+                         LDS_AS char *vw) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+        mfma_phase<D, 0>(kc, vp, off, qf, pu, s0, s1, acc);
+        __builtin_amdgcn_s_setprio(0);
+        finish(t, kw, vw);
     };
 
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, (const LDS_AS char *)K1.b, (const LDS_AS char *)V0.b, (LDS_AS char *)K0.b,
-             (LDS_AS char *)V1.b);
-        if (t + 1 < ntiles)
-            step(t + 1, (const LDS_AS char *)K0.b, (const LDS_AS char *)V1.b, (LDS_AS char *)K1.b,
-                 (LDS_AS char *)V0.b);
+    // The lagging waves load K(1) and V(0), then pass one extra barrier: from
+    // here on they run one phase behind the leading waves.
+    if (lag) {
+        if (ntiles > 1) kload.load((LDS_AS char *)K1.b, khead, kKeyTile, T);
+        vload.load((LDS_AS char *)V0.b, vhead, 0, T);
+        __syncthreads();
     }
+    // Tile 0 has no P V yet; tiles alternate buffers K0/V1 (even) and K1/V0 (odd).
+    __builtin_amdgcn_s_setprio(1);
+    mfma_phase<D, 1>((const LDS_AS char *)K0.b, nullptr, off, qf, pu, s0, s1, acc);
+    __builtin_amdgcn_s_setprio(0);
+    finish(0, (LDS_AS char *)K0.b, (LDS_AS char *)V1.b);
+    for (int t = 1; t < ntiles; t += 2) {
+        iteration(t, (const LDS_AS char *)K1.b, (const LDS_AS char *)V0.b, (LDS_AS char *)K1.b,
+                  (LDS_AS char *)V0.b);
+        if (t + 1 < ntiles)
+            iteration(t + 1, (const LDS_AS char *)K0.b, (const LDS_AS char *)V1.b,
+                      (LDS_AS char *)K0.b, (LDS_AS char *)V1.b);
+    }
+    // P V of the last tile, then the leading waves pass their extra barrier.
+    __builtin_amdgcn_s_setprio(1);
+    if ((ntiles - 1) & 1) mfma_phase<D, 2>(nullptr, (const LDS_AS char *)V1.b, off, qf, pu, s0, s1, acc);
+    else mfma_phase<D, 2>(nullptr, (const LDS_AS char *)V0.b, off, qf, pu, s0, s1, acc);
+    __builtin_amdgcn_s_setprio(0);
+    if (!lag) __syncthreads();
 
     // Epilogue: O = acc / l, rounded once to bf16; lse = ln 2 * (m + log2 l).
     const float l_tot = l_run + __shfl_xor(l_run, 32);
