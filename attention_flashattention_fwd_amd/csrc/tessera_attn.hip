@@ -159,6 +159,19 @@ struct TileLoader {
     }
 };
 
+// Workgroup barrier without a memory fence.  __syncthreads() also waits for
+// every outstanding memory operation of the wave, including the direct
+// global->LDS loads issued for the next tiles, which would serialise them.
+// Here every LDS write is such a load and is waited for explicitly (vmcnt)
+// before the barrier that publishes it, and every LDS read is consumed within
+// its phase; the empty asm statements only stop the compiler from moving LDS
+// accesses across the barrier.
+__device__ __forceinline__ void phase_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void wait_dma_and_barrier() {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS loads have landed
     __syncthreads();                      // ... and everyone else's
@@ -292,7 +305,7 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS c
 // array.
 template <int D>
 __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
-    __shared__ LdsTile<D> K0, K1, V0, V1;
+    __shared__ LdsTile<D> K0, K1, K2, V0, V1, V2;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -325,7 +338,13 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     const int kv_end = causal ? q_end : T;
     const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
 
-    TileLoader<D, false, kWaves>(w, lane).load((LDS_AS char *)K0.b, khead, 0, T);
+    // Prologue loads, shared by all waves: K(0), K(1), V(0).
+    {
+        const TileLoader<D, false, kWaves> kl(w, lane);
+        kl.load((LDS_AS char *)K0.b, khead, 0, T);
+        if (ntiles > 1) kl.load((LDS_AS char *)K1.b, khead, kKeyTile, T);
+        TileLoader<D, true, kWaves>(w, lane).load((LDS_AS char *)V0.b, vhead, 0, T);
+    }
 
     // Q fragment (B operand of S^T = K Q^T): lane holds 8 dims of its query
     // row per 16-dim step.  Rows past T are clamped; their results are dropped.
@@ -351,12 +370,10 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     f32x16 s0 = f32x16{}, s1 = f32x16{};   // scores of the tile in flight
     u32x4 pu[4];                           // its probabilities, bf16, per 16-key step
 
-    wait_dma_and_barrier();
-
     const LaneOffsets<D> off(lane);
-    // Loaders of the lagging waves (they issue every K/V load after the first).
-    const TileLoader<D, false, 4> kload(w & 3, lane);
-    const TileLoader<D, true, 4> vload(w & 3, lane);
+    // Every wave issues its share (1/8) of each later K/V tile load.
+    const TileLoader<D, false, kWaves> kload(w, lane);
+    const TileLoader<D, true, kWaves> vload(w, lane);
     // Vector phase of tile t: mask, online softmax, P(t).
     auto softmax_phase = [&](int t) __attribute__((always_inline)) {
         const int j0 = t * kKeyTile;
@@ -408,54 +425,55 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
             pu[2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
         }
     };
-    // Iteration t of every wave: the MFMA phase of tile t (S(t) from kc, and
-    // P(t-1) V(t-1) from vp), a barrier, the vector phase of tile t, a barrier.
-    // The lagging waves also issue the loads of K(t+2) into kw and V(t+1) into
-    // vw during their vector phase and wait for them at the end of their next
-    // MFMA phase; by then both buffers' previous tiles have been read.
+    // Iteration t of every wave: the MFMA phase of tile t (S(t) from K(t), and
+    // P(t-1) V(t-1)), a barrier, the vector phase of tile t, a barrier.  Tile j
+    // lives in LDS buffers K[j%3] and V[j%3]; each tile is loaded in two
+    // halves.  In its vector phase of tile t a wave first waits for its
+    // previous loads, then issues new ones: the leading waves (phase 2t+1) their
+    // halves of K(t+2) and V(t+1), the lagging waves (phase 2t+2) their halves
+    // of K(t+3) and V(t+2).  Each target buffer's previous tile was last read in
+    // phase 2t+1 or earlier, and each half lands two phases after it is issued,
+    // before the barrier that precedes its first read.
     auto finish = [&](int t, LDS_AS char *kw, LDS_AS char *vw) __attribute__((always_inline)) {
-        if (lag) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): its loads have landed
-        __syncthreads();
+        phase_barrier();
         softmax_phase(t);
-        if (lag) {
-            if (t + 2 < ntiles) kload.load(kw, khead, (t + 2) * kKeyTile, T);
-            if (t + 1 < ntiles) vload.load(vw, vhead, (t + 1) * kKeyTile, T);
-        }
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's previous loads landed
+        const int tk = t + (lag ? 3 : 2), tv = t + (lag ? 2 : 1);
+        if (tk < ntiles) kload.load(kw, khead, tk * kKeyTile, T);
+        if (tv < ntiles) vload.load(vw, vhead, tv * kKeyTile, T);
+        phase_barrier();
     };
     auto iteration = [&](int t, const LDS_AS char *kc, const LDS_AS char *vp, LDS_AS char *kw,
                          LDS_AS char *vw) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_setprio(1);
         mfma_phase<D, 0>(kc, vp, off, qf, pu, s0, s1, acc);
-        __builtin_amdgcn_s_setprio(0);
         finish(t, kw, vw);
     };
+    LDS_AS char *kb[3] = {(LDS_AS char *)K0.b, (LDS_AS char *)K1.b, (LDS_AS char *)K2.b};
+    LDS_AS char *vb[3] = {(LDS_AS char *)V0.b, (LDS_AS char *)V1.b, (LDS_AS char *)V2.b};
 
-    // The lagging waves load K(1) and V(0), then pass one extra barrier: from
-    // here on they run one phase behind the leading waves.
+    // The lagging waves also load their halves of K(2) and V(1), then pass one
+    // extra barrier: from here on they run one phase behind the leading waves.
+    wait_dma_and_barrier();
     if (lag) {
-        if (ntiles > 1) kload.load((LDS_AS char *)K1.b, khead, kKeyTile, T);
-        vload.load((LDS_AS char *)V0.b, vhead, 0, T);
-        __syncthreads();
+        if (ntiles > 2) kload.load(kb[2], khead, 2 * kKeyTile, T);
+        if (ntiles > 1) vload.load(vb[1], vhead, kKeyTile, T);
+        phase_barrier();
     }
-    // Tile 0 has no P V yet; tiles alternate buffers K0/V1 (even) and K1/V0 (odd).
-    __builtin_amdgcn_s_setprio(1);
-    mfma_phase<D, 1>((const LDS_AS char *)K0.b, nullptr, off, qf, pu, s0, s1, acc);
-    __builtin_amdgcn_s_setprio(0);
-    finish(0, (LDS_AS char *)K0.b, (LDS_AS char *)V1.b);
-    for (int t = 1; t < ntiles; t += 2) {
-        iteration(t, (const LDS_AS char *)K1.b, (const LDS_AS char *)V0.b, (LDS_AS char *)K1.b,
-                  (LDS_AS char *)V0.b);
-        if (t + 1 < ntiles)
-            iteration(t + 1, (const LDS_AS char *)K0.b, (const LDS_AS char *)V1.b,
-                      (LDS_AS char *)K0.b, (LDS_AS char *)V1.b);
+    // Tile 0 has no P V yet.  Buffers written in iteration t (r = t % 3):
+    // leading waves K[(r+2)%3], V[(r+1)%3]; lagging waves K[r], V[(r+2)%3].
+    mfma_phase<D, 1>(kb[0], nullptr, off, qf, pu, s0, s1, acc);
+    finish(0, lag ? kb[0] : kb[2], lag ? vb[2] : vb[1]);
+    for (int t = 1; t < ntiles; t += 3) {
+        iteration(t, kb[1], vb[0], lag ? kb[1] : kb[0], lag ? vb[0] : vb[2]);
+        if (t + 1 < ntiles) iteration(t + 1, kb[2], vb[1], lag ? kb[2] : kb[1], lag ? vb[1] : vb[0]);
+        if (t + 2 < ntiles) iteration(t + 2, kb[0], vb[2], lag ? kb[0] : kb[2], lag ? vb[2] : vb[1]);
     }
     // P V of the last tile, then the leading waves pass their extra barrier.
-    __builtin_amdgcn_s_setprio(1);
-    if ((ntiles - 1) & 1) mfma_phase<D, 2>(nullptr, (const LDS_AS char *)V1.b, off, qf, pu, s0, s1, acc);
-    else mfma_phase<D, 2>(nullptr, (const LDS_AS char *)V0.b, off, qf, pu, s0, s1, acc);
-    __builtin_amdgcn_s_setprio(0);
-    if (!lag) __syncthreads();
+    const int last = (ntiles - 1) % 3;
+    if (last == 0) mfma_phase<D, 2>(nullptr, vb[0], off, qf, pu, s0, s1, acc);
+    else if (last == 1) mfma_phase<D, 2>(nullptr, vb[1], off, qf, pu, s0, s1, acc);
+    else mfma_phase<D, 2>(nullptr, vb[2], off, qf, pu, s0, s1, acc);
+    if (!lag) phase_barrier();
 
     // Epilogue: O = acc / l, rounded once to bf16; lse = ln 2 * (m + log2 l).
     const float l_tot = l_run + __shfl_xor(l_run, 32);
