@@ -46,10 +46,14 @@ constexpr double kLog2e = 1.442695040888963407;
 constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kKeyTile = 64;              // keys per staged K/V tile
-// The running maximum is only raised when a tile's maximum exceeds it by more
-// than this (log2 units).  Any stale maximum gives the same result: it cancels
-// between the numerator and the row sum; it only bounds p by 2^8.
-constexpr float kRescaleSlack = 8.0f;
+// The running maximum m is only raised when some p = 2^(s*c - m) of a tile
+// would exceed 2^kRescaleSlack.  Any stale maximum gives the same result: it
+// cancels between the numerator and the row sum.  The bound keeps every p,
+// and the fp32 sums over up to 2^31 keys, far from overflow, and makes a
+// raise rare once the first tile has set m.
+constexpr int kRescaleSlack = 32;
+constexpr float kRescaleBound = 4294967296.0f;   // 2^kRescaleSlack
+static_assert(kRescaleBound == (float)(1ull << kRescaleSlack), "bound mismatch");
 
 // LDS chunk swizzles (16-byte chunks of a D-wide bf16 row).  K is read as
 // 16-byte MFMA operands, one key row per lane; V is read with transposing
@@ -138,6 +142,15 @@ struct TileLoader {
     __device__ __forceinline__ bool active(int r) const {
         return kLoadsPerTile % NW == 0 || wi + NW * r < kLoadsPerTile;
     }
+    // Load r alone, for the tile whose row 0 is at base; rows past `last`
+    // (T - 1 - j0, which may exceed the tile) are clamped to row `last`.
+    __device__ __forceinline__ void load_one(int r, LDS_AS char *dst, const char *base,
+                                             int last) const {
+        if (!active(r)) return;
+        const int key = (int)(off[r] / kRowBytes);
+        const uint32_t o = (uint32_t)(min(key, last) - key) * kRowBytes + off[r];
+        dma16(base, o, (uint32_t)(uintptr_t)dst + 1024 * (wi + NW * r));
+    }
     __device__ __forceinline__ void load(LDS_AS char *dst, const uint16_t *head, int j0,
                                          int T) const {
         const char *base = (const char *)(head + (int64_t)j0 * D);
@@ -159,17 +172,58 @@ struct TileLoader {
     }
 };
 
+// The K/V loads that ride in one MFMA phase: this wave's share of one K tile
+// and one V tile, issued in kSteps single loads spread over the phase.  Step 0
+// first waits for the loads this wave issued in its previous MFMA phase.
+template <int D>
+struct PhaseLoads {
+    static constexpr int kPer = TileLoader<D, false, kWaves>::kPerWave;
+    static constexpr int kSteps = 2 * kPer;
+    const TileLoader<D, false, kWaves> &kl;
+    const TileLoader<D, true, kWaves> &vl;
+    LDS_AS char *kdst, *vdst;
+    const char *ksrc, *vsrc;
+    int klast, vlast;
+    __device__ __forceinline__ void step(int s) const {
+        if (s == 0) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        if (s < kPer) kl.load_one(s, kdst, ksrc, klast);
+        else vl.load_one(s - kPer, vdst, vsrc, vlast);
+    }
+};
+struct NoLoads {
+    static constexpr int kSteps = 0;
+    __device__ __forceinline__ void step(int) const {}
+};
+
 // Workgroup barrier without a memory fence.  __syncthreads() also waits for
 // every outstanding memory operation of the wave, including the direct
 // global->LDS loads issued for the next tiles, which would serialise them.
 // Here every LDS write is such a load and is waited for explicitly (vmcnt)
 // before the barrier that publishes it, and every LDS read is consumed within
-// its phase; the empty asm statements only stop the compiler from moving LDS
-// accesses across the barrier.
+// its phase.  The empty asm statements stop the compiler from moving memory
+// accesses across the barrier, the scheduling barriers any other instruction:
+// each phase's MFMA or vector work stays inside its phase.
 __device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Pins a vector phase's results to the end of that phase.  P and the row sum
+// feed only later code, so without this the compiler may sink their exp2 and
+// convert work past the barrier into the wave's own MFMA phase.
+__device__ __forceinline__ void settle(const u32x4 (&pu)[4], const float (&l)[4]) {
+    asm volatile("" ::"v"(pu[0]), "v"(pu[1]), "v"(pu[2]), "v"(pu[3]), "v"(l[0]), "v"(l[1]),
+                 "v"(l[2]), "v"(l[3]));
+}
+
+// max(x, x of lane l ^ 32): a swap of the wave's halves, without LDS.
+__device__ __forceinline__ float max_with_partner(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ void wait_dma_and_barrier() {
@@ -239,10 +293,11 @@ __device__ __forceinline__ void schedule_mfma_phase() {
     }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, class Loads>
 __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS char *vt,
                                            const LaneOffsets<D> &off, const bf16x8 *qf,
-                                           const u32x4 *pu, f32x16 &s0, f32x16 &s1, f32x16 *acc) {
+                                           const u32x4 *pu, f32x16 &s0, f32x16 &s1, f32x16 *acc,
+                                           const Loads &loads) {
     constexpr int kRowBytes = D * 2;
     constexpr int kHalf = D / 8;                         // MFMAs of each kind
     constexpr int kN = MODE == 0 ? 2 * kHalf : kHalf;    // MFMAs in this phase
@@ -281,6 +336,12 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS c
             const int st = j / (D / 32), db = j % (D / 32);
             acc[db] = mfma32(__builtin_bit_cast(bf16x8, cur), __builtin_bit_cast(bf16x8, pu[st]),
                              acc[db]);
+        }
+        // The phase's K/V loads, one after each of kSteps evenly spaced ops.
+        if constexpr (Loads::kSteps > 0) {
+#pragma unroll
+            for (int st = 0; st < Loads::kSteps; ++st)
+                if (i == kN * (2 * st + 1) / (2 * Loads::kSteps)) loads.step(st);
         }
     }
     schedule_mfma_phase<MODE, 0, kN>();
@@ -364,9 +425,8 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
     float m_run = -INFINITY;   // running max of scale*log2(e)*s (log2 units)
-    float l_run = 0.f;         // this lane's share of the running row sum
+    float l_run[4] = {0.f, 0.f, 0.f, 0.f};   // this lane's share of the row sum, 4 parts
     const float c = a.c;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     f32x16 s0 = f32x16{}, s1 = f32x16{};   // scores of the tile in flight
     u32x4 pu[4];                           // its probabilities, bf16, per 16-key step
 
@@ -389,94 +449,132 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
                 if (r + 32 > last) s1[i] = -INFINITY;
             }
         }
-        // Online softmax, in log2 units; the running max only moves when a
-        // tile beats it by more than kRescaleSlack.
-        float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s0[1], s1[1]);
+        // Online softmax, in log2 units, with a lazy running max m.  P =
+        // 2^(s*c - m) is computed with the current m before the tile has been
+        // looked at; m only has to move when some p of the tile exceeds
+        // 2^kRescaleSlack (or overflowed), which the lane sees in its own row
+        // sum.  Any lane that asks for a move makes the whole wave take the
+        // branch, which takes the tile max over both lanes of each query row
+        // (so both keep the same m), rescales the accumulators and recomputes
+        // P.  Every p is at most 2^kRescaleSlack.
+        f32x16 e0, e1;
+        float ls[4];
+        auto sweep = [&]() __attribute__((always_inline)) {
+            const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-        for (int i = 2; i < 16; i += 2) {
-            ma = fmaxf(fmaxf(ma, s0[i]), s1[i]);
-            mb = fmaxf(fmaxf(mb, s0[i + 1]), s1[i + 1]);
-        }
-        float mx = fmaxf(ma, mb);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_tile = mx * c;
-        if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
-            const float m_new = fmaxf(m_run, m_tile);
+            for (int i = 0; i < 16; ++i) {
+                e0[i] = __builtin_fmaf(s0[i], c, -m_sub);
+                e1[i] = __builtin_fmaf(s1[i], c, -m_sub);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                e0[i] = __builtin_amdgcn_exp2f(e0[i]);
+                e1[i] = __builtin_amdgcn_exp2f(e1[i]);
+            }
+            // Row sums in fp32, four partial sums.  Plain adds: the bf16
+            // dot-product instruction would stall behind the partner wave's
+            // MFMAs.
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ls[k] = e0[k] + e1[k];
+#pragma unroll
+            for (int i = 4; i < 16; ++i) {
+                ls[i & 3] += e0[i];
+                ls[i & 3] += e1[i];
+            }
+        };
+        sweep();
+        const float l_tile = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        if (__builtin_amdgcn_ballot_w64(!(l_tile <= kRescaleBound) || m_run == -INFINITY) != 0) {
+            float mq[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = 4 * k;
+                float m = fmaxf(fmaxf(s0[i], s0[i + 1]), s0[i + 2]);
+                m = fmaxf(fmaxf(m, s0[i + 3]), s1[i]);
+                m = fmaxf(fmaxf(m, s1[i + 1]), s1[i + 2]);
+                mq[k] = fmaxf(m, s1[i + 3]);
+            }
+            const float m_own = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])) * c;
+            const float m_new = fmaxf(m_run, max_with_partner(m_own));
             const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) l_run[k] *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
             m_run = m_new;
+            sweep();
         }
-        const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
-        // P = 2^(s*c - m) rounded to bf16; the row sum adds the rounded values.
+#pragma unroll
+        for (int k = 0; k < 4; ++k) l_run[k] += ls[k];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            f32x2 x0, x1;
-            x0[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * e], c, -m_sub));
-            x0[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * e + 1], c, -m_sub));
-            x1[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * e], c, -m_sub));
-            x1[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * e + 1], c, -m_sub));
-            const bf16x2 p0 = __builtin_convertvector(x0, bf16x2);
-            const bf16x2 p1 = __builtin_convertvector(x1, bf16x2);
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, l_run, false);
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, l_run, false);
+            const bf16x2 p0 = __builtin_convertvector((f32x2){e0[2 * e], e0[2 * e + 1]}, bf16x2);
+            const bf16x2 p1 = __builtin_convertvector((f32x2){e1[2 * e], e1[2 * e + 1]}, bf16x2);
             pu[e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p0);
             pu[2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
         }
     };
     // Iteration t of every wave: the MFMA phase of tile t (S(t) from K(t), and
     // P(t-1) V(t-1)), a barrier, the vector phase of tile t, a barrier.  Tile j
-    // lives in LDS buffers K[j%3] and V[j%3]; each tile is loaded in two
-    // halves.  In its vector phase of tile t a wave first waits for its
-    // previous loads, then issues new ones: the leading waves (phase 2t+1) their
-    // halves of K(t+2) and V(t+1), the lagging waves (phase 2t+2) their halves
-    // of K(t+3) and V(t+2).  Each target buffer's previous tile was last read in
-    // phase 2t+1 or earlier, and each half lands two phases after it is issued,
-    // before the barrier that precedes its first read.
-    auto finish = [&](int t, LDS_AS char *kw, LDS_AS char *vw) __attribute__((always_inline)) {
+    // lives in LDS buffers K[j%3] and V[j%3].  The MFMA phase of tile t also
+    // carries the wave's share of the loads of K(t+2) and V(t+1): the leading
+    // waves issue theirs in phase 2t, the lagging waves in phase 2t+1.  The
+    // target buffers held K(t-1) and V(t-2), last read in phase 2t-1; each
+    // wave waits for its loads in its next MFMA phase, before the barrier
+    // that ends phase 2t+3, and the first read of either tile is in phase
+    // 2t+4.  Near the end the tile index is clamped to the last tile: such a
+    // load refills a buffer that is never read again.
+    auto loads = [&](int t, LDS_AS char *kw, LDS_AS char *vw) __attribute__((always_inline)) {
+        const int tk = min(t + 2, ntiles - 1), tv = min(t + 1, ntiles - 1);
+        return PhaseLoads<D>{kload,
+                             vload,
+                             kw,
+                             vw,
+                             (const char *)(khead + (int64_t)tk * kKeyTile * D),
+                             (const char *)(vhead + (int64_t)tv * kKeyTile * D),
+                             T - 1 - tk * kKeyTile,
+                             T - 1 - tv * kKeyTile};
+    };
+    auto finish = [&](int t) __attribute__((always_inline)) {
         phase_barrier();
         softmax_phase(t);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's previous loads landed
-        const int tk = t + (lag ? 3 : 2), tv = t + (lag ? 2 : 1);
-        if (tk < ntiles) kload.load(kw, khead, tk * kKeyTile, T);
-        if (tv < ntiles) vload.load(vw, vhead, tv * kKeyTile, T);
+        settle(pu, l_run);
         phase_barrier();
     };
     auto iteration = [&](int t, const LDS_AS char *kc, const LDS_AS char *vp, LDS_AS char *kw,
                          LDS_AS char *vw) __attribute__((always_inline)) {
-        mfma_phase<D, 0>(kc, vp, off, qf, pu, s0, s1, acc);
-        finish(t, kw, vw);
+        mfma_phase<D, 0>(kc, vp, off, qf, pu, s0, s1, acc, loads(t, kw, vw));
+        finish(t);
     };
     LDS_AS char *kb[3] = {(LDS_AS char *)K0.b, (LDS_AS char *)K1.b, (LDS_AS char *)K2.b};
     LDS_AS char *vb[3] = {(LDS_AS char *)V0.b, (LDS_AS char *)V1.b, (LDS_AS char *)V2.b};
 
-    // The lagging waves also load their halves of K(2) and V(1), then pass one
-    // extra barrier: from here on they run one phase behind the leading waves.
+    // The lagging waves pass one extra barrier: from here on they run one
+    // phase behind the leading waves.
     wait_dma_and_barrier();
-    if (lag) {
-        if (ntiles > 2) kload.load(kb[2], khead, 2 * kKeyTile, T);
-        if (ntiles > 1) vload.load(vb[1], vhead, kKeyTile, T);
-        phase_barrier();
-    }
-    // Tile 0 has no P V yet.  Buffers written in iteration t (r = t % 3):
-    // leading waves K[(r+2)%3], V[(r+1)%3]; lagging waves K[r], V[(r+2)%3].
-    mfma_phase<D, 1>(kb[0], nullptr, off, qf, pu, s0, s1, acc);
-    finish(0, lag ? kb[0] : kb[2], lag ? vb[2] : vb[1]);
+    if (lag) phase_barrier();
+    // Tile 0 has no P V yet.
+    mfma_phase<D, 1>(kb[0], nullptr, off, qf, pu, s0, s1, acc, loads(0, kb[2], vb[1]));
+    finish(0);
     for (int t = 1; t < ntiles; t += 3) {
-        iteration(t, kb[1], vb[0], lag ? kb[1] : kb[0], lag ? vb[0] : vb[2]);
-        if (t + 1 < ntiles) iteration(t + 1, kb[2], vb[1], lag ? kb[2] : kb[1], lag ? vb[1] : vb[0]);
-        if (t + 2 < ntiles) iteration(t + 2, kb[0], vb[2], lag ? kb[0] : kb[2], lag ? vb[2] : vb[1]);
+        iteration(t, kb[1], vb[0], kb[0], vb[2]);
+        if (t + 1 < ntiles) iteration(t + 1, kb[2], vb[1], kb[1], vb[0]);
+        if (t + 2 < ntiles) iteration(t + 2, kb[0], vb[2], kb[2], vb[1]);
     }
     // P V of the last tile, then the leading waves pass their extra barrier.
     const int last = (ntiles - 1) % 3;
-    if (last == 0) mfma_phase<D, 2>(nullptr, vb[0], off, qf, pu, s0, s1, acc);
-    else if (last == 1) mfma_phase<D, 2>(nullptr, vb[1], off, qf, pu, s0, s1, acc);
-    else mfma_phase<D, 2>(nullptr, vb[2], off, qf, pu, s0, s1, acc);
+    const NoLoads none;
+    if (last == 0) mfma_phase<D, 2>(nullptr, vb[0], off, qf, pu, s0, s1, acc, none);
+    else if (last == 1) mfma_phase<D, 2>(nullptr, vb[1], off, qf, pu, s0, s1, acc, none);
+    else mfma_phase<D, 2>(nullptr, vb[2], off, qf, pu, s0, s1, acc, none);
     if (!lag) phase_barrier();
+    // The clamped loads of the last phases must land before the workgroup's
+    // LDS is released.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // Epilogue: O = acc / l, rounded once to bf16; lse = ln 2 * (m + log2 l).
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_own = (l_run[0] + l_run[1]) + (l_run[2] + l_run[3]);
+    const float l_tot = l_own + __shfl_xor(l_own, 32);
     if (query < T) {
         const float inv = 1.f / l_tot;
         uint16_t *dst = a.o + (q_row0 + query) * D;
