@@ -266,7 +266,7 @@ struct LaneOffsets {
 // software pipeline.  The D/8 score MFMAs and D/8 P V MFMAs alternate, and the
 // LDS operands are read kPrefetch MFMAs ahead.  MODE: 0 both, 1 scores only
 // (first tile), 2 P V only (after the last tile).
-constexpr int kPrefetch = 4;
+constexpr int kPrefetch = 3;
 
 // LDS reads feeding op i of an MFMA phase: one 16-byte read for a score MFMA,
 // two transposing 8-byte reads for a P V MFMA.
@@ -274,61 +274,98 @@ constexpr int phase_reads(int mode, int i) {
     return (mode == 1 || (mode == 0 && (i & 1) == 0)) ? 1 : 2;
 }
 
-// Scheduling groups for the MFMA phase: the reads of the first kPrefetch ops,
-// then for every op its MFMA followed by the reads of the op kPrefetch later.
-// This pins the prefetch distance that the plain schedule would shrink.
-template <int MODE, int I, int N>
+// Row sums of P on the matrix cores (ones x P^T, four MFMAs per tile) instead
+// of 32 vector adds: for D < 128 the MFMA phase is the shorter one.
+template <int D>
+constexpr bool kRowSumOnMfma = D < 128;
+
+// Whether the MFMA phase runs at raised issue priority, so that the matrix-core
+// wave wins issue conflicts with the vector wave: for D = 128 the MFMA phase
+// is the longer one, for D < 128 the vector phase is.
+template <int D>
+constexpr bool kMfmaPriority = D == 128;
+
+// Scheduling groups for the MFMA phase: the row-sum MFMAs first (they need no
+// LDS operand), then for every op its MFMA followed by the reads of the op
+// kPrefetch later (the first kPrefetch ops' operands arrive preloaded).  This
+// pins the prefetch distance that the plain schedule would shrink.
+template <int MODE, int I, int N, bool SUM>
 __device__ __forceinline__ void schedule_mfma_phase() {
-    if constexpr (I == 0) {
-        constexpr int pre = N < kPrefetch ? N : kPrefetch;
-        [&]<int... J>(std::integer_sequence<int, J...>) {
-            (__builtin_amdgcn_sched_group_barrier(0x100, phase_reads(MODE, J), 0), ...);
-        }(std::make_integer_sequence<int, pre>{});
-    }
+    if constexpr (I == 0 && SUM) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if constexpr (I < N) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if constexpr (I + kPrefetch < N)
             __builtin_amdgcn_sched_group_barrier(0x100, phase_reads(MODE, I + kPrefetch), 0);
-        schedule_mfma_phase<MODE, I + 1, N>();
+        schedule_mfma_phase<MODE, I + 1, N, false>();
     }
 }
 
+// Op i of an MFMA phase: whether it is a score MFMA, and its index among the
+// ops of its kind.
+template <int MODE>
+__device__ __forceinline__ constexpr bool op_is_score(int i) {
+    return MODE == 1 || (MODE == 0 && (i & 1) == 0);
+}
+template <int MODE>
+__device__ __forceinline__ constexpr int op_index(int i) {
+    return MODE == 0 ? (i >> 1) : i;
+}
+
+// The LDS operand of op i: a K row chunk (score MFMA, tile kt) or two
+// transposing reads of V (P V MFMA, tile vt).
+template <int D, int MODE>
+__device__ __forceinline__ u32x4 phase_operand(const LDS_AS char *kt, const LDS_AS char *vt,
+                                               const LaneOffsets<D> &off, int i) {
+    constexpr int kRowBytes = D * 2;
+    const int j = op_index<MODE>(i);
+    if (op_is_score<MODE>(i)) {
+        const int ks = j >> 1, kb = j & 1;
+        return *(const LDS_AS u32x4 *)(kt + off.k[ks] + kb * 32 * kRowBytes);
+    }
+    const int st = j / (D / 32), db = j % (D / 32);
+    const LDS_AS char *p = vt + off.v[db] + st * 16 * kRowBytes;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p);
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(p + 8 * kRowBytes));
+    return __builtin_bit_cast(u32x4, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Reads the operands of the first kPrefetch ops of an MFMA phase, ahead of it.
+template <int D, int MODE>
+__device__ __forceinline__ void preload(const LDS_AS char *kt, const LDS_AS char *vt,
+                                        const LaneOffsets<D> &off, u32x4 (&ring)[kPrefetch]) {
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) ring[i] = phase_operand<D, MODE>(kt, vt, off, i);
+}
+
+// The phase itself; `ring` holds the operands of its first kPrefetch ops.
 template <int D, int MODE, class Loads>
 __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS char *vt,
                                            const LaneOffsets<D> &off, const bf16x8 *qf,
                                            const u32x4 *pu, f32x16 &s0, f32x16 &s1, f32x16 *acc,
-                                           const Loads &loads) {
-    constexpr int kRowBytes = D * 2;
+                                           f32x16 &lsum, const Loads &loads,
+                                           u32x4 (&ring)[kPrefetch]) {
     constexpr int kHalf = D / 8;                         // MFMAs of each kind
     constexpr int kN = MODE == 0 ? 2 * kHalf : kHalf;    // MFMAs in this phase
-    // op i -> (is_score, index j within its kind)
-    auto is_score = [](int i) { return MODE == 1 || (MODE == 0 && (i & 1) == 0); };
-    auto index = [](int i) { return MODE == 0 ? (i >> 1) : i; };
-    auto load = [&](int i) __attribute__((always_inline)) -> u32x4 {
-        const int j = index(i);
-        if (is_score(i)) {
-            const int ks = j >> 1, kb = j & 1;
-            return *(const LDS_AS u32x4 *)(kt + off.k[ks] + kb * 32 * kRowBytes);
-        }
-        const int st = j / (D / 32), db = j % (D / 32);
-        const LDS_AS char *p = vt + off.v[db] + st * 16 * kRowBytes;
-        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p);
-        const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(p + 8 * kRowBytes));
-        return __builtin_bit_cast(u32x4, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
+    static_assert(kN >= kPrefetch, "phase shorter than the prefetch ring");
+    if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(2);
     if (MODE != 2) {
         s0 = f32x16{};
         s1 = f32x16{};
     }
-    u32x4 ring[kPrefetch];
+    constexpr bool kSum = kRowSumOnMfma<D> && MODE != 1;
+    if constexpr (kSum) {
+        const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                             (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) ring[i] = load(i);
+        for (int st = 0; st < 4; ++st) lsum = mfma32(ones, __builtin_bit_cast(bf16x8, pu[st]), lsum);
+    }
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
         const u32x4 cur = ring[i % kPrefetch];
-        if (i + kPrefetch < kN) ring[i % kPrefetch] = load(i + kPrefetch);
-        const int j = index(i);
-        if (is_score(i)) {
+        if (i + kPrefetch < kN)
+            ring[i % kPrefetch] = phase_operand<D, MODE>(kt, vt, off, i + kPrefetch);
+        const int j = op_index<MODE>(i);
+        if (op_is_score<MODE>(i)) {
             const int ks = j >> 1;
             if ((j & 1) == 0) s0 = mfma32(__builtin_bit_cast(bf16x8, cur), qf[ks], s0);
             else s1 = mfma32(__builtin_bit_cast(bf16x8, cur), qf[ks], s1);
@@ -344,7 +381,8 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS c
                 if (i == kN * (2 * st + 1) / (2 * Loads::kSteps)) loads.step(st);
         }
     }
-    schedule_mfma_phase<MODE, 0, kN>();
+    schedule_mfma_phase<MODE, 0, kN, kSum>();
+    if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(0);
 }
 
 // Work split.  A workgroup owns one query tile of 32*nqb rows for hg query
@@ -366,7 +404,7 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS c
 // array.
 template <int D>
 __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
-    __shared__ LdsTile<D> K0, K1, K2, V0, V1, V2;
+    __shared__ LdsTile<D> K0, K1, K2, K3, V0, V1, V2, V3;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -399,12 +437,15 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     const int kv_end = causal ? q_end : T;
     const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
 
-    // Prologue loads, shared by all waves: K(0), K(1), V(0).
+    // Prologue loads, shared by all waves: K(0), K(1), K(2), V(0), V(1).
     {
         const TileLoader<D, false, kWaves> kl(w, lane);
+        const TileLoader<D, true, kWaves> vl(w, lane);
         kl.load((LDS_AS char *)K0.b, khead, 0, T);
         if (ntiles > 1) kl.load((LDS_AS char *)K1.b, khead, kKeyTile, T);
-        TileLoader<D, true, kWaves>(w, lane).load((LDS_AS char *)V0.b, vhead, 0, T);
+        if (ntiles > 2) kl.load((LDS_AS char *)K2.b, khead, 2 * kKeyTile, T);
+        vl.load((LDS_AS char *)V0.b, vhead, 0, T);
+        if (ntiles > 1) vl.load((LDS_AS char *)V1.b, vhead, kKeyTile, T);
     }
 
     // Q fragment (B operand of S^T = K Q^T): lane holds 8 dims of its query
@@ -426,6 +467,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
     float m_run = -INFINITY;   // running max of scale*log2(e)*s (log2 units)
     float l_run[4] = {0.f, 0.f, 0.f, 0.f};   // this lane's share of the row sum, 4 parts
+    f32x16 lsum = f32x16{};   // row sums from the matrix cores (every entry the full sum)
     const float c = a.c;
     f32x16 s0 = f32x16{}, s1 = f32x16{};   // scores of the tile in flight
     u32x4 pu[4];                           // its probabilities, bf16, per 16-key step
@@ -451,12 +493,13 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
         }
         // Online softmax, in log2 units, with a lazy running max m.  P =
         // 2^(s*c - m) is computed with the current m before the tile has been
-        // looked at; m only has to move when some p of the tile exceeds
-        // 2^kRescaleSlack (or overflowed), which the lane sees in its own row
-        // sum.  Any lane that asks for a move makes the whole wave take the
-        // branch, which takes the tile max over both lanes of each query row
-        // (so both keep the same m), rescales the accumulators and recomputes
-        // P.  Every p is at most 2^kRescaleSlack.
+        // looked at; m only has to move when some p of the tile would exceed
+        // 2^kRescaleSlack.  The lane tests that on its own row sum when it
+        // forms one (D = 128), else on its own tile max.  Any lane that asks
+        // for a move makes the whole wave take the branch, which takes the
+        // tile max over both lanes of each query row (so both keep the same
+        // m), rescales the accumulators and recomputes P.  Every p is at most
+        // 2^kRescaleSlack.
         f32x16 e0, e1;
         float ls[4];
         auto sweep = [&]() __attribute__((always_inline)) {
@@ -471,20 +514,20 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
                 e0[i] = __builtin_amdgcn_exp2f(e0[i]);
                 e1[i] = __builtin_amdgcn_exp2f(e1[i]);
             }
-            // Row sums in fp32, four partial sums.  Plain adds: the bf16
-            // dot-product instruction would stall behind the partner wave's
-            // MFMAs.
+            if constexpr (!kRowSumOnMfma<D>) {
+                // Row sums in fp32, four partial sums.  Plain adds: the bf16
+                // dot-product instruction would stall behind the partner
+                // wave's MFMAs.
 #pragma unroll
-            for (int k = 0; k < 4; ++k) ls[k] = e0[k] + e1[k];
+                for (int k = 0; k < 4; ++k) ls[k] = e0[k] + e1[k];
 #pragma unroll
-            for (int i = 4; i < 16; ++i) {
-                ls[i & 3] += e0[i];
-                ls[i & 3] += e1[i];
+                for (int i = 4; i < 16; ++i) {
+                    ls[i & 3] += e0[i];
+                    ls[i & 3] += e1[i];
+                }
             }
         };
-        sweep();
-        const float l_tile = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-        if (__builtin_amdgcn_ballot_w64(!(l_tile <= kRescaleBound) || m_run == -INFINITY) != 0) {
+        auto own_max = [&]() __attribute__((always_inline)) {
             float mq[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -494,18 +537,31 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
                 m = fmaxf(fmaxf(m, s1[i + 1]), s1[i + 2]);
                 mq[k] = fmaxf(m, s1[i + 3]);
             }
-            const float m_own = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])) * c;
+            return fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])) * c;
+        };
+        auto move_max = [&](float m_own) __attribute__((always_inline)) {
             const float m_new = fmaxf(m_run, max_with_partner(m_own));
             const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
             for (int k = 0; k < 4; ++k) l_run[k] *= alpha;
+            lsum[0] *= alpha;   // the only entry read
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
             m_run = m_new;
             sweep();
-        }
+        };
+        sweep();
+        if constexpr (kRowSumOnMfma<D>) {
+            const float m_own = own_max();
+            if (__builtin_amdgcn_ballot_w64(m_own > m_run + (float)kRescaleSlack) != 0)
+                move_max(m_own);
+        } else {
+            const float l_tile = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            if (__builtin_amdgcn_ballot_w64(!(l_tile <= kRescaleBound) || m_run == -INFINITY) != 0)
+                move_max(own_max());
 #pragma unroll
-        for (int k = 0; k < 4; ++k) l_run[k] += ls[k];
+            for (int k = 0; k < 4; ++k) l_run[k] += ls[k];
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const bf16x2 p0 = __builtin_convertvector((f32x2){e0[2 * e], e0[2 * e + 1]}, bf16x2);
@@ -516,16 +572,18 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     };
     // Iteration t of every wave: the MFMA phase of tile t (S(t) from K(t), and
     // P(t-1) V(t-1)), a barrier, the vector phase of tile t, a barrier.  Tile j
-    // lives in LDS buffers K[j%3] and V[j%3].  The MFMA phase of tile t also
-    // carries the wave's share of the loads of K(t+2) and V(t+1): the leading
+    // lives in LDS buffers K[j%4] and V[j%4].  The MFMA phase of tile t also
+    // carries the wave's share of the loads of K(t+3) and V(t+2): the leading
     // waves issue theirs in phase 2t, the lagging waves in phase 2t+1.  The
     // target buffers held K(t-1) and V(t-2), last read in phase 2t-1; each
-    // wave waits for its loads in its next MFMA phase, before the barrier
-    // that ends phase 2t+3, and the first read of either tile is in phase
-    // 2t+4.  Near the end the tile index is clamped to the last tile: such a
-    // load refills a buffer that is never read again.
+    // wave waits for its loads in its next MFMA phase, so both halves are
+    // published by the barrier that ends phase 2t+3.  The vector phase of
+    // tile t (phase 2t+1 or 2t+2) reads the first operands of the next MFMA
+    // phase, K(t+1) and V(t), published by the end of phase 2t-1.  Near the
+    // end the tile index of a load is clamped to the last tile: such a load
+    // refills a buffer that is never read again.
     auto loads = [&](int t, LDS_AS char *kw, LDS_AS char *vw) __attribute__((always_inline)) {
-        const int tk = min(t + 2, ntiles - 1), tv = min(t + 1, ntiles - 1);
+        const int tk = min(t + 3, ntiles - 1), tv = min(t + 2, ntiles - 1);
         return PhaseLoads<D>{kload,
                              vload,
                              kw,
@@ -535,46 +593,62 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
                              T - 1 - tk * kKeyTile,
                              T - 1 - tv * kKeyTile};
     };
-    auto finish = [&](int t) __attribute__((always_inline)) {
+    u32x4 ring[kPrefetch];   // operands of the next MFMA phase's first ops
+    auto finish = [&](int t, const LDS_AS char *kn, const LDS_AS char *vn)
+                      __attribute__((always_inline)) {
         phase_barrier();
+        if (t + 1 < ntiles) preload<D, 0>(kn, vn, off, ring);
+        else preload<D, 2>(nullptr, vn, off, ring);
         softmax_phase(t);
         settle(pu, l_run);
         phase_barrier();
     };
     auto iteration = [&](int t, const LDS_AS char *kc, const LDS_AS char *vp, LDS_AS char *kw,
-                         LDS_AS char *vw) __attribute__((always_inline)) {
-        mfma_phase<D, 0>(kc, vp, off, qf, pu, s0, s1, acc, loads(t, kw, vw));
-        finish(t);
+                         LDS_AS char *vw, const LDS_AS char *kn, const LDS_AS char *vn)
+                         __attribute__((always_inline)) {
+        mfma_phase<D, 0>(kc, vp, off, qf, pu, s0, s1, acc, lsum, loads(t, kw, vw), ring);
+        finish(t, kn, vn);
     };
-    LDS_AS char *kb[3] = {(LDS_AS char *)K0.b, (LDS_AS char *)K1.b, (LDS_AS char *)K2.b};
-    LDS_AS char *vb[3] = {(LDS_AS char *)V0.b, (LDS_AS char *)V1.b, (LDS_AS char *)V2.b};
+    LDS_AS char *kb[4] = {(LDS_AS char *)K0.b, (LDS_AS char *)K1.b, (LDS_AS char *)K2.b,
+                          (LDS_AS char *)K3.b};
+    LDS_AS char *vb[4] = {(LDS_AS char *)V0.b, (LDS_AS char *)V1.b, (LDS_AS char *)V2.b,
+                          (LDS_AS char *)V3.b};
 
     // The lagging waves pass one extra barrier: from here on they run one
     // phase behind the leading waves.
     wait_dma_and_barrier();
+    preload<D, 1>(kb[0], nullptr, off, ring);
     if (lag) phase_barrier();
     // Tile 0 has no P V yet.
-    mfma_phase<D, 1>(kb[0], nullptr, off, qf, pu, s0, s1, acc, loads(0, kb[2], vb[1]));
-    finish(0);
-    for (int t = 1; t < ntiles; t += 3) {
-        iteration(t, kb[1], vb[0], kb[0], vb[2]);
-        if (t + 1 < ntiles) iteration(t + 1, kb[2], vb[1], kb[1], vb[0]);
-        if (t + 2 < ntiles) iteration(t + 2, kb[0], vb[2], kb[2], vb[1]);
+    mfma_phase<D, 1>(kb[0], nullptr, off, qf, pu, s0, s1, acc, lsum, loads(0, kb[3], vb[2]),
+                     ring);
+    finish(0, kb[1], vb[0]);
+    for (int t = 1; t < ntiles; t += 4) {
+        iteration(t, kb[1], vb[0], kb[0], vb[3], kb[2], vb[1]);
+        if (t + 1 < ntiles) iteration(t + 1, kb[2], vb[1], kb[1], vb[0], kb[3], vb[2]);
+        if (t + 2 < ntiles) iteration(t + 2, kb[3], vb[2], kb[2], vb[1], kb[0], vb[3]);
+        if (t + 3 < ntiles) iteration(t + 3, kb[0], vb[3], kb[3], vb[2], kb[1], vb[0]);
     }
     // P V of the last tile, then the leading waves pass their extra barrier.
-    const int last = (ntiles - 1) % 3;
+    const int last = (ntiles - 1) % 4;
     const NoLoads none;
-    if (last == 0) mfma_phase<D, 2>(nullptr, vb[0], off, qf, pu, s0, s1, acc, none);
-    else if (last == 1) mfma_phase<D, 2>(nullptr, vb[1], off, qf, pu, s0, s1, acc, none);
-    else mfma_phase<D, 2>(nullptr, vb[2], off, qf, pu, s0, s1, acc, none);
+    if (last == 0) mfma_phase<D, 2>(nullptr, vb[0], off, qf, pu, s0, s1, acc, lsum, none, ring);
+    else if (last == 1) mfma_phase<D, 2>(nullptr, vb[1], off, qf, pu, s0, s1, acc, lsum, none, ring);
+    else if (last == 2) mfma_phase<D, 2>(nullptr, vb[2], off, qf, pu, s0, s1, acc, lsum, none, ring);
+    else mfma_phase<D, 2>(nullptr, vb[3], off, qf, pu, s0, s1, acc, lsum, none, ring);
     if (!lag) phase_barrier();
     // The clamped loads of the last phases must land before the workgroup's
     // LDS is released.
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // Epilogue: O = acc / l, rounded once to bf16; lse = ln 2 * (m + log2 l).
-    const float l_own = (l_run[0] + l_run[1]) + (l_run[2] + l_run[3]);
-    const float l_tot = l_own + __shfl_xor(l_own, 32);
+    float l_tot;
+    if constexpr (kRowSumOnMfma<D>) {
+        l_tot = lsum[0];
+    } else {
+        const float l_own = (l_run[0] + l_run[1]) + (l_run[2] + l_run[3]);
+        l_tot = l_own + __shfl_xor(l_own, 32);
+    }
     if (query < T) {
         const float inv = 1.f / l_tot;
         uint16_t *dst = a.o + (q_row0 + query) * D;
