@@ -8,8 +8,8 @@
 //     run on v_mfma_f32_32x32x16_bf16 in a transposed form, S^T = K Q^T and
 //     O^T = V^T P^T, so that every lane owns one query row: the softmax row
 //     statistics live in a lane (plus its partner lane 32 away) instead of
-//     being spread over the wave.  K/V tiles are staged through LDS, double
-//     buffered, and one staged tile serves the query heads of a GQA group.
+//     being spread over the wave.  K/V tiles are staged through a four-deep
+//     LDS ring, and one staged tile serves the query heads of a GQA group.
 //   * attn_fwd_f32_kernel -- fp32 inputs, computed on the vector ALUs in fp32.
 #include <hip/hip_runtime.h>
 
@@ -397,11 +397,10 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS c
 // P(t) = 2^(S c - m) in bf16), separated by barriers.  Waves 0-3 and 4-7 (one
 // of each per SIMD) run the same code one phase apart -- waves 4-7 pass one
 // extra barrier first -- so in every phase one wave of a SIMD feeds the matrix
-// cores while the other works the vector ALUs.  K(t) and V(t-1) stay in LDS
-// for phases 2t and 2t+1; the lagging waves stream K(t+1) and V(t) in with
-// direct global->LDS loads during phase 2t and wait for them at the end of
-// phase 2t+1.  The loop is unrolled by two so every LDS buffer is a distinct
-// array.
+// cores while the other works the vector ALUs.  K/V tiles stream into a
+// four-deep LDS ring with direct global->LDS loads issued between the MFMAs;
+// the schedule of loads, waits and reads is spelled out at the loop below,
+// which is unrolled by four so every LDS buffer is a distinct array.
 template <int D>
 __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     __shared__ LdsTile<D> K0, K1, K2, K3, V0, V1, V2, V3;
