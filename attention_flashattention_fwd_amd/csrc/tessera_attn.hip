@@ -108,10 +108,13 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t 
 }
 #pragma clang diagnostic pop
 
-// One K or V tile in LDS: kKeyTile rows of D bf16, 16-byte chunks swizzled.
+// The LDS ring: four K tiles, then four V tiles, each kKeyTile rows of D bf16
+// in swizzled 16-byte chunks.
 template <int D>
-struct LdsTile {
-    __attribute__((aligned(16))) char b[kKeyTile * D * 2];
+struct LdsRing {
+    static constexpr int kTileBytes = kKeyTile * D * 2;
+    __attribute__((aligned(16))) char k[4][kTileBytes];
+    __attribute__((aligned(16))) char v[4][kTileBytes];
 };
 
 // The loads that copy key rows [j0, j0 + kKeyTile) of one K or V head into an
@@ -142,13 +145,18 @@ struct TileLoader {
     __device__ __forceinline__ bool active(int r) const {
         return kLoadsPerTile % NW == 0 || wi + NW * r < kLoadsPerTile;
     }
-    // Load r alone, for the tile whose row 0 is at base; rows past `last`
-    // (T - 1 - j0, which may exceed the tile) are clamped to row `last`.
+    // Load r alone, for the tile whose row 0 is at base.  With CLAMP, rows past
+    // `last` (T - 1 - j0, which may exceed the tile) are clamped to row `last`;
+    // without, the caller guarantees that every row of the tile is below T.
+    template <bool CLAMP>
     __device__ __forceinline__ void load_one(int r, LDS_AS char *dst, const char *base,
                                              int last) const {
         if (!active(r)) return;
-        const int key = (int)(off[r] / kRowBytes);
-        const uint32_t o = (uint32_t)(min(key, last) - key) * kRowBytes + off[r];
+        uint32_t o = off[r];
+        if constexpr (CLAMP) {
+            const int key = (int)(off[r] / kRowBytes);
+            o += (uint32_t)(min(key, last) - key) * kRowBytes;
+        }
         dma16(base, o, (uint32_t)(uintptr_t)dst + 1024 * (wi + NW * r));
     }
     __device__ __forceinline__ void load(LDS_AS char *dst, const uint16_t *head, int j0,
@@ -175,7 +183,8 @@ struct TileLoader {
 // The K/V loads that ride in one MFMA phase: this wave's share of one K tile
 // and one V tile, issued in kSteps single loads spread over the phase.  Step 0
 // first waits for the loads this wave issued in its previous MFMA phase.
-template <int D>
+// RAGGED: T is not a multiple of the key tile, so a tile may cross T.
+template <int D, bool RAGGED>
 struct PhaseLoads {
     static constexpr int kPer = TileLoader<D, false, kWaves>::kPerWave;
     static constexpr int kSteps = 2 * kPer;
@@ -186,8 +195,8 @@ struct PhaseLoads {
     int klast, vlast;
     __device__ __forceinline__ void step(int s) const {
         if (s == 0) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        if (s < kPer) kl.load_one(s, kdst, ksrc, klast);
-        else vl.load_one(s - kPer, vdst, vsrc, vlast);
+        if (s < kPer) kl.template load_one<RAGGED>(s, kdst, ksrc, klast);
+        else vl.template load_one<RAGGED>(s - kPer, vdst, vsrc, vlast);
     }
 };
 struct NoLoads {
@@ -245,8 +254,8 @@ __device__ __forceinline__ void wait_dma_and_barrier() {
 template <int D>
 struct LaneOffsets {
     int k[D / 16];
-    int v[D / 32];
-    __device__ __forceinline__ LaneOffsets(int lane) {
+    uint32_t v[D / 32];       // LDS byte addresses within V buffer 0
+    __device__ __forceinline__ LaneOffsets(int lane, const LDS_AS char *v0) {
         constexpr int kRowBytes = D * 2;
         const int col = lane & 31, hi = lane >> 5, grp = lane >> 4, s16 = lane & 15;
 #pragma unroll
@@ -256,7 +265,11 @@ struct LaneOffsets {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
             const int d = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
-            v[db] = r * kRowBytes + (((d >> 3) ^ swz_v<D>(r)) << 4) + (d & 7) * 2;
+            v[db] = (uint32_t)(uintptr_t)v0 + r * kRowBytes + (((d >> 3) ^ swz_v<D>(r)) << 4) +
+                    (d & 7) * 2;
+            // Opaque to the compiler: a V read is then this register plus an
+            // immediate offset (the buffer and row step, < 64 KB), with no add.
+            asm("" : "+v"(v[db]));
         }
     }
 };
@@ -311,10 +324,10 @@ __device__ __forceinline__ constexpr int op_index(int i) {
     return MODE == 0 ? (i >> 1) : i;
 }
 
-// The LDS operand of op i: a K row chunk (score MFMA, tile kt) or two
-// transposing reads of V (P V MFMA, tile vt).
+// The LDS operand of op i: a K row chunk (score MFMA, K tile kt) or two
+// transposing reads of V (P V MFMA, V tile at byte offset vrel from V buffer 0).
 template <int D, int MODE>
-__device__ __forceinline__ u32x4 phase_operand(const LDS_AS char *kt, const LDS_AS char *vt,
+__device__ __forceinline__ u32x4 phase_operand(const LDS_AS char *kt, uint32_t vrel,
                                                const LaneOffsets<D> &off, int i) {
     constexpr int kRowBytes = D * 2;
     const int j = op_index<MODE>(i);
@@ -323,7 +336,8 @@ __device__ __forceinline__ u32x4 phase_operand(const LDS_AS char *kt, const LDS_
         return *(const LDS_AS u32x4 *)(kt + off.k[ks] + kb * 32 * kRowBytes);
     }
     const int st = j / (D / 32), db = j % (D / 32);
-    const LDS_AS char *p = vt + off.v[db] + st * 16 * kRowBytes;
+    const LDS_AS char *p =
+        (const LDS_AS char *)(uintptr_t)(off.v[db] + vrel + st * 16 * kRowBytes);
     const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p);
     const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(p + 8 * kRowBytes));
     return __builtin_bit_cast(u32x4, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -331,15 +345,15 @@ __device__ __forceinline__ u32x4 phase_operand(const LDS_AS char *kt, const LDS_
 
 // Reads the operands of the first kPrefetch ops of an MFMA phase, ahead of it.
 template <int D, int MODE>
-__device__ __forceinline__ void preload(const LDS_AS char *kt, const LDS_AS char *vt,
+__device__ __forceinline__ void preload(const LDS_AS char *kt, uint32_t vrel,
                                         const LaneOffsets<D> &off, u32x4 (&ring)[kPrefetch]) {
 #pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) ring[i] = phase_operand<D, MODE>(kt, vt, off, i);
+    for (int i = 0; i < kPrefetch; ++i) ring[i] = phase_operand<D, MODE>(kt, vrel, off, i);
 }
 
 // The phase itself; `ring` holds the operands of its first kPrefetch ops.
 template <int D, int MODE, class Loads>
-__device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS char *vt,
+__device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, uint32_t vrel,
                                            const LaneOffsets<D> &off, const bf16x8 *qf,
                                            const u32x4 *pu, f32x16 &s0, f32x16 &s1, f32x16 *acc,
                                            f32x16 &lsum, const Loads &loads,
@@ -363,7 +377,7 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS c
     for (int i = 0; i < kN; ++i) {
         const u32x4 cur = ring[i % kPrefetch];
         if (i + kPrefetch < kN)
-            ring[i % kPrefetch] = phase_operand<D, MODE>(kt, vt, off, i + kPrefetch);
+            ring[i % kPrefetch] = phase_operand<D, MODE>(kt, vrel, off, i + kPrefetch);
         const int j = op_index<MODE>(i);
         if (op_is_score<MODE>(i)) {
             const int ks = j >> 1;
@@ -401,9 +415,10 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, const LDS_AS c
 // four-deep LDS ring with direct global->LDS loads issued between the MFMAs;
 // the schedule of loads, waits and reads is spelled out at the loop below,
 // which is unrolled by four so every LDS buffer is a distinct array.
-template <int D>
+// RAGGED: T % kKeyTile != 0 (the last key tile crosses T).
+template <int D, bool RAGGED>
 __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
-    __shared__ LdsTile<D> K0, K1, K2, K3, V0, V1, V2, V3;
+    __shared__ LdsRing<D> lds;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -440,11 +455,11 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     {
         const TileLoader<D, false, kWaves> kl(w, lane);
         const TileLoader<D, true, kWaves> vl(w, lane);
-        kl.load((LDS_AS char *)K0.b, khead, 0, T);
-        if (ntiles > 1) kl.load((LDS_AS char *)K1.b, khead, kKeyTile, T);
-        if (ntiles > 2) kl.load((LDS_AS char *)K2.b, khead, 2 * kKeyTile, T);
-        vl.load((LDS_AS char *)V0.b, vhead, 0, T);
-        if (ntiles > 1) vl.load((LDS_AS char *)V1.b, vhead, kKeyTile, T);
+        kl.load((LDS_AS char *)lds.k[0], khead, 0, T);
+        if (ntiles > 1) kl.load((LDS_AS char *)lds.k[1], khead, kKeyTile, T);
+        if (ntiles > 2) kl.load((LDS_AS char *)lds.k[2], khead, 2 * kKeyTile, T);
+        vl.load((LDS_AS char *)lds.v[0], vhead, 0, T);
+        if (ntiles > 1) vl.load((LDS_AS char *)lds.v[1], vhead, kKeyTile, T);
     }
 
     // Q fragment (B operand of S^T = K Q^T): lane holds 8 dims of its query
@@ -471,7 +486,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     f32x16 s0 = f32x16{}, s1 = f32x16{};   // scores of the tile in flight
     u32x4 pu[4];                           // its probabilities, bf16, per 16-key step
 
-    const LaneOffsets<D> off(lane);
+    const LaneOffsets<D> off(lane, (const LDS_AS char *)lds.v[0]);
     // Every wave issues its share (1/8) of each later K/V tile load.
     const TileLoader<D, false, kWaves> kload(w, lane);
     const TileLoader<D, true, kWaves> vload(w, lane);
@@ -479,7 +494,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     auto softmax_phase = [&](int t) __attribute__((always_inline)) {
         const int j0 = t * kKeyTile;
         // Mask keys hidden from a query (diagonal tile) or past T (ragged tile).
-        if ((j0 + kKeyTile > T) || (causal && j0 + kKeyTile - 1 > qw0)) {
+        if ((RAGGED && j0 + kKeyTile > T) || (causal && j0 + kKeyTile - 1 > qw0)) {
             // Row i of this lane is key j0 + 4*hi + 8*(i/4) + i%4 (+32 in s1);
             // it is visible iff that key <= last, the last key this query sees.
             const int last = (causal ? min(query, T - 1) : T - 1) - j0 - 4 * hi;
@@ -583,7 +598,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     // refills a buffer that is never read again.
     auto loads = [&](int t, LDS_AS char *kw, LDS_AS char *vw) __attribute__((always_inline)) {
         const int tk = min(t + 3, ntiles - 1), tv = min(t + 2, ntiles - 1);
-        return PhaseLoads<D>{kload,
+        return PhaseLoads<D, RAGGED>{kload,
                              vload,
                              kw,
                              vw,
@@ -593,48 +608,49 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
                              T - 1 - tv * kKeyTile};
     };
     u32x4 ring[kPrefetch];   // operands of the next MFMA phase's first ops
-    auto finish = [&](int t, const LDS_AS char *kn, const LDS_AS char *vn)
-                      __attribute__((always_inline)) {
+    // Buffers are named by index: K tile b at lds.k[b], V tile b at byte offset
+    // b * kTileBytes from V buffer 0 (a compile-time constant in every read).
+    constexpr uint32_t kTB = LdsRing<D>::kTileBytes;
+    auto kbuf = [&](int b) __attribute__((always_inline)) { return (LDS_AS char *)lds.k[b]; };
+    auto vbuf = [&](int b) __attribute__((always_inline)) { return (LDS_AS char *)lds.v[b]; };
+    auto finish = [&](int t, int kn, int vn) __attribute__((always_inline)) {
         phase_barrier();
-        if (t + 1 < ntiles) preload<D, 0>(kn, vn, off, ring);
-        else preload<D, 2>(nullptr, vn, off, ring);
+        if (t + 1 < ntiles) preload<D, 0>(kbuf(kn), vn * kTB, off, ring);
+        else preload<D, 2>(nullptr, vn * kTB, off, ring);
         softmax_phase(t);
         settle(pu, l_run);
         phase_barrier();
     };
-    auto iteration = [&](int t, const LDS_AS char *kc, const LDS_AS char *vp, LDS_AS char *kw,
-                         LDS_AS char *vw, const LDS_AS char *kn, const LDS_AS char *vn)
+    // Iteration t: K(t) in buffer kc, V(t-1) in vp; loads into kw, vw; the
+    // next phase's K(t+1) in kn, V(t) in vn.
+    auto iteration = [&](int t, int kc, int vp, int kw, int vw, int kn, int vn)
                          __attribute__((always_inline)) {
-        mfma_phase<D, 0>(kc, vp, off, qf, pu, s0, s1, acc, lsum, loads(t, kw, vw), ring);
+        mfma_phase<D, 0>(kbuf(kc), vp * kTB, off, qf, pu, s0, s1, acc, lsum,
+                         loads(t, kbuf(kw), vbuf(vw)), ring);
         finish(t, kn, vn);
     };
-    LDS_AS char *kb[4] = {(LDS_AS char *)K0.b, (LDS_AS char *)K1.b, (LDS_AS char *)K2.b,
-                          (LDS_AS char *)K3.b};
-    LDS_AS char *vb[4] = {(LDS_AS char *)V0.b, (LDS_AS char *)V1.b, (LDS_AS char *)V2.b,
-                          (LDS_AS char *)V3.b};
 
     // The lagging waves pass one extra barrier: from here on they run one
     // phase behind the leading waves.
     wait_dma_and_barrier();
-    preload<D, 1>(kb[0], nullptr, off, ring);
+    preload<D, 1>(kbuf(0), 0, off, ring);
     if (lag) phase_barrier();
     // Tile 0 has no P V yet.
-    mfma_phase<D, 1>(kb[0], nullptr, off, qf, pu, s0, s1, acc, lsum, loads(0, kb[3], vb[2]),
-                     ring);
-    finish(0, kb[1], vb[0]);
+    mfma_phase<D, 1>(kbuf(0), 0, off, qf, pu, s0, s1, acc, lsum, loads(0, kbuf(3), vbuf(2)), ring);
+    finish(0, 1, 0);
     for (int t = 1; t < ntiles; t += 4) {
-        iteration(t, kb[1], vb[0], kb[0], vb[3], kb[2], vb[1]);
-        if (t + 1 < ntiles) iteration(t + 1, kb[2], vb[1], kb[1], vb[0], kb[3], vb[2]);
-        if (t + 2 < ntiles) iteration(t + 2, kb[3], vb[2], kb[2], vb[1], kb[0], vb[3]);
-        if (t + 3 < ntiles) iteration(t + 3, kb[0], vb[3], kb[3], vb[2], kb[1], vb[0]);
+        iteration(t, 1, 0, 0, 3, 2, 1);
+        if (t + 1 < ntiles) iteration(t + 1, 2, 1, 1, 0, 3, 2);
+        if (t + 2 < ntiles) iteration(t + 2, 3, 2, 2, 1, 0, 3);
+        if (t + 3 < ntiles) iteration(t + 3, 0, 3, 3, 2, 1, 0);
     }
     // P V of the last tile, then the leading waves pass their extra barrier.
     const int last = (ntiles - 1) % 4;
     const NoLoads none;
-    if (last == 0) mfma_phase<D, 2>(nullptr, vb[0], off, qf, pu, s0, s1, acc, lsum, none, ring);
-    else if (last == 1) mfma_phase<D, 2>(nullptr, vb[1], off, qf, pu, s0, s1, acc, lsum, none, ring);
-    else if (last == 2) mfma_phase<D, 2>(nullptr, vb[2], off, qf, pu, s0, s1, acc, lsum, none, ring);
-    else mfma_phase<D, 2>(nullptr, vb[3], off, qf, pu, s0, s1, acc, lsum, none, ring);
+    if (last == 0) mfma_phase<D, 2>(nullptr, 0 * kTB, off, qf, pu, s0, s1, acc, lsum, none, ring);
+    else if (last == 1) mfma_phase<D, 2>(nullptr, 1 * kTB, off, qf, pu, s0, s1, acc, lsum, none, ring);
+    else if (last == 2) mfma_phase<D, 2>(nullptr, 2 * kTB, off, qf, pu, s0, s1, acc, lsum, none, ring);
+    else mfma_phase<D, 2>(nullptr, 3 * kTB, off, qf, pu, s0, s1, acc, lsum, none, ring);
     if (!lag) phase_barrier();
     // The clamped loads of the last phases must land before the workgroup's
     // LDS is released.
@@ -809,12 +825,18 @@ extern "C" int tessera_attn_fwd(const void *q, const void *k, const void *v, voi
     a.c = scale == 0.f ? 1.0f : (float)(fabs((double)scale) * kLog2e);
 
     hipStream_t s = (hipStream_t)stream;
-    if (D == 128)
-        hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-    else if (D == 64)
-        hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(attn_fwd_bf16_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    const dim3 g((unsigned)grid), blk(kThreads);
+    const bool ragged = T % kKeyTile != 0;
+    if (D == 128) {
+        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), g, blk, 0, s, a);
+    } else if (D == 64) {
+        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), g, blk, 0, s, a);
+    } else {
+        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<32, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<32, false>), g, blk, 0, s, a);
+    }
     return launch_status();
 }
 
