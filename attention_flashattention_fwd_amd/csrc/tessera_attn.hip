@@ -292,11 +292,6 @@ constexpr int phase_reads(int mode, int i) {
 template <int D>
 constexpr bool kRowSumOnMfma = D < 128;
 
-// Whether the MFMA phase runs at raised issue priority, so that the matrix-core
-// wave wins issue conflicts with the vector wave: for D = 128 the MFMA phase
-// is the longer one, for D < 128 the vector phase is.
-template <int D>
-constexpr bool kMfmaPriority = D == 128;
 
 // Scheduling groups for the MFMA phase: the row-sum MFMAs first (they need no
 // LDS operand), then for every op its MFMA followed by the reads of the op
@@ -361,7 +356,6 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, uint32_t vrel,
     constexpr int kHalf = D / 8;                         // MFMAs of each kind
     constexpr int kN = MODE == 0 ? 2 * kHalf : kHalf;    // MFMAs in this phase
     static_assert(kN >= kPrefetch, "phase shorter than the prefetch ring");
-    if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(2);
     if (MODE != 2) {
         s0 = f32x16{};
         s1 = f32x16{};
@@ -396,7 +390,6 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, uint32_t vrel,
         }
     }
     schedule_mfma_phase<MODE, 0, kN, kSum>();
-    if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(0);
 }
 
 // Work split.  A workgroup owns one query tile of 32*nqb rows for hg query
@@ -491,7 +484,8 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     const TileLoader<D, false, kWaves> kload(w, lane);
     const TileLoader<D, true, kWaves> vload(w, lane);
     // Vector phase of tile t: mask, online softmax, P(t).
-    auto softmax_phase = [&](int t) __attribute__((always_inline)) {
+    // `first`: tile 0 (m is still -inf there; afterwards m is finite).
+    auto softmax_phase = [&](int t, bool first) __attribute__((always_inline)) {
         const int j0 = t * kKeyTile;
         // Mask keys hidden from a query (diagonal tile) or past T (ragged tile).
         if ((RAGGED && j0 + kKeyTile > T) || (causal && j0 + kKeyTile - 1 > qw0)) {
@@ -513,11 +507,10 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
         // for a move makes the whole wave take the branch, which takes the
         // tile max over both lanes of each query row (so both keep the same
         // m), rescales the accumulators and recomputes P.  Every p is at most
-        // 2^kRescaleSlack.
+        // 2^kRescaleSlack.  Tile 0 always takes the branch.
         f32x16 e0, e1;
         float ls[4];
-        auto sweep = [&]() __attribute__((always_inline)) {
-            const float m_sub = (m_run == -INFINITY) ? 0.f : m_run;
+        auto sweep = [&](float m_sub) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 e0[i] = __builtin_fmaf(s0[i], c, -m_sub);
@@ -562,16 +555,16 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
             m_run = m_new;
-            sweep();
+            sweep(m_new == -INFINITY ? 0.f : m_new);
         };
-        sweep();
+        sweep(first ? 0.f : m_run);
         if constexpr (kRowSumOnMfma<D>) {
             const float m_own = own_max();
-            if (__builtin_amdgcn_ballot_w64(m_own > m_run + (float)kRescaleSlack) != 0)
+            if (first || __builtin_amdgcn_ballot_w64(m_own > m_run + (float)kRescaleSlack) != 0)
                 move_max(m_own);
         } else {
             const float l_tile = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-            if (__builtin_amdgcn_ballot_w64(!(l_tile <= kRescaleBound) || m_run == -INFINITY) != 0)
+            if (first || __builtin_amdgcn_ballot_w64(!(l_tile <= kRescaleBound)) != 0)
                 move_max(own_max());
 #pragma unroll
             for (int k = 0; k < 4; ++k) l_run[k] += ls[k];
@@ -613,11 +606,11 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     constexpr uint32_t kTB = LdsRing<D>::kTileBytes;
     auto kbuf = [&](int b) __attribute__((always_inline)) { return (LDS_AS char *)lds.k[b]; };
     auto vbuf = [&](int b) __attribute__((always_inline)) { return (LDS_AS char *)lds.v[b]; };
-    auto finish = [&](int t, int kn, int vn) __attribute__((always_inline)) {
+    auto finish = [&](int t, int kn, int vn, bool first) __attribute__((always_inline)) {
         phase_barrier();
         if (t + 1 < ntiles) preload<D, 0>(kbuf(kn), vn * kTB, off, ring);
         else preload<D, 2>(nullptr, vn * kTB, off, ring);
-        softmax_phase(t);
+        softmax_phase(t, first);
         settle(pu, l_run);
         phase_barrier();
     };
@@ -627,7 +620,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
                          __attribute__((always_inline)) {
         mfma_phase<D, 0>(kbuf(kc), vp * kTB, off, qf, pu, s0, s1, acc, lsum,
                          loads(t, kbuf(kw), vbuf(vw)), ring);
-        finish(t, kn, vn);
+        finish(t, kn, vn, false);
     };
 
     // The lagging waves pass one extra barrier: from here on they run one
@@ -637,7 +630,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     if (lag) phase_barrier();
     // Tile 0 has no P V yet.
     mfma_phase<D, 1>(kbuf(0), 0, off, qf, pu, s0, s1, acc, lsum, loads(0, kbuf(3), vbuf(2)), ring);
-    finish(0, 1, 0);
+    finish(0, 1, 0, true);
     for (int t = 1; t < ntiles; t += 4) {
         iteration(t, 1, 0, 0, 3, 2, 1);
         if (t + 1 < ntiles) iteration(t + 1, 2, 1, 1, 0, 3, 2);
