@@ -97,6 +97,42 @@ def test_edge_shapes_bf16(B, Hq, Hkv, T, D, causal):
     full_case(B, Hq, Hkv, T, D, "bf16", causal, seed=T)
 
 
+# T a multiple of the 64-key tile: the kernel variant without the row clamp on
+# K/V loads, with 1..9 tiles so that every position of the four-deep LDS ring
+# ends a run, and each head grouping (G = 4, 3, 6, 1 and 2).
+ALIGNED = [
+    (1, 8, 2, 64, 128, True),     # one tile
+    (2, 8, 2, 128, 64, True),
+    (1, 4, 1, 192, 32, True),
+    (1, 8, 2, 256, 128, False),
+    (2, 6, 2, 320, 64, True),     # G=3
+    (1, 12, 2, 384, 128, True),   # G=6
+    (1, 4, 4, 576, 64, False),    # MHA
+    (1, 4, 2, 448, 32, False),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D,causal", ALIGNED)
+def test_aligned_shapes_bf16(B, Hq, Hkv, T, D, causal):
+    full_case(B, Hq, Hkv, T, D, "bf16", causal, seed=T + 1)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_scores_growing_along_the_keys(D):
+    """Key rows grow with position, so later tiles beat the running max by far
+    more than the lazy-rescale bound: the rescale path runs mid-sequence."""
+    B, Hq, Hkv, T = 1, 8, 2, 512
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, T, D, "bf16", seed=5)
+    grow = (1.0 + torch.arange(T, dtype=torch.float32) / 8.0).view(1, 1, T, 1)
+    k = (k.float() * grow).to(torch.bfloat16)
+    scale = inputs.default_scale(D)
+    say(f"case growing keys B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
+    o, l = run_gpu(q, k, v, True, scale)
+    O_ref, l_ref = oracle.attn_fwd(inputs.bits(q), inputs.bits(k), inputs.bits(v), True, scale)
+    check_close(o, l, O_ref, l_ref, "bf16")
+    assert l_ref.max() - l_ref.min() > 64 * math.log(2)   # the spread that forces rescales
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,T,D,causal", [
     (1, 2, 1, 1, 32, True), (2, 4, 2, 65, 64, True), (1, 4, 4, 130, 128, False),
     (1, 8, 2, 300, 128, True), (2, 2, 2, 77, 32, False)])
