@@ -88,23 +88,25 @@ def recorded_traffic():
 
 
 def time_steps(torch, fn, steps, warmup, stream):
-    """W untimed steps, then K timed steps bracketed by synchronisation; the
-    GPU time of the K steps comes from HIP events on the kernel's stream."""
+    """W untimed steps, then K timed steps bracketed by synchronisation.  HIP
+    events on the kernel's stream sit between consecutive launches, so besides
+    the mean GPU time of the K steps the per-launch median and minimum come
+    out of the same run."""
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
+        events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        start.record(stream)
-        for _ in range(steps):
+        events[0].record(stream)
+        for i in range(steps):
             fn()
-        stop.record(stream)
+            events[i + 1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(stop) / steps
-    return gpu_ms, wall * 1e3 / steps
+    per = sorted(events[i].elapsed_time(events[i + 1]) for i in range(steps))
+    gpu_ms = events[0].elapsed_time(events[steps]) / steps
+    return gpu_ms, wall * 1e3 / steps, per[len(per) // 2], per[0]
 
 
 def cpu_baseline(w, q, k, v, out, lse, budget_s):
@@ -200,8 +202,8 @@ def main(argv=None):
         a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
         b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
         c = torch.empty_like(a)
-        gemm_ms, _ = time_steps(torch, lambda: torch.matmul(a, b, out=c), max(1, args.steps),
-                                args.warmup, stream)
+        gemm_ms, _, _, _ = time_steps(torch, lambda: torch.matmul(a, b, out=c),
+                                      max(1, args.steps), args.warmup, stream)
         tflops = 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12
         print(json.dumps({"gemm_calibration": f"bf16 {n}x{n}x{n} torch.matmul",
                           "ms_per_call": round(gemm_ms, 4), "tflops": round(tflops, 1),
@@ -218,8 +220,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         fn = lambda: binding.attn_fwd_into(qd, kd, vd, out, lse, w.causal, w.scale,  # noqa: E731
                                            stream=stream)
-        gpu_ms, wall_ms = time_steps(torch, fn, steps, warmup, stream)
-        res = {"w": w, "gpu_ms": gpu_ms, "wall_ms": wall_ms}
+        gpu_ms, wall_ms, med_ms, min_ms = time_steps(torch, fn, steps, warmup, stream)
+        res = {"w": w, "gpu_ms": gpu_ms, "wall_ms": wall_ms, "med_ms": med_ms, "min_ms": min_ms}
         if with_cpu:
             res["cpu"], res["parity"] = cpu_baseline(w, q, k, v, out, lse, args.cpu_seconds)
         return res
@@ -239,6 +241,7 @@ def main(argv=None):
             secondary[name] = {
                 "config": r["w"].describe(),
                 "us_per_call": round(r["gpu_ms"] * 1e3, 2),
+                "us_median": round(r["med_ms"] * 1e3, 2),
                 "tflops": round(r["w"].flops / (r["gpu_ms"] * 1e-3) / 1e12, 1),
                 "pct_of_peak": round(100 * r["w"].flops / (r["gpu_ms"] * 1e-3) / 1e12
                                      / PEAK_BF16_TFLOPS, 2),
@@ -267,11 +270,20 @@ def main(argv=None):
             "traffic": traffic,
             "kernel": f"attn_fwd_bf16_kernel<{w.D}>",
             "kernel_us_per_launch": round(head["gpu_ms"] * 1e3, 2),
+            "kernel_us_median": round(head["med_ms"] * 1e3, 2),
+            "kernel_us_min": round(head["min_ms"] * 1e3, 2),
         },
     }
     if counters:
         line["roofline"]["counters"] = counters
         line["roofline"]["hbm_gbs"] = round(traffic / (head["gpu_ms"] * 1e-3) / 1e9, 1)
+        if "shader_clock_ghz" in counters:
+            # the same 4096 flop/clk/CU at the clock the profiled run measured
+            at_clock = 256 * 4096 * counters["shader_clock_ghz"] * 1e9 / 1e12
+            line["roofline"]["frac_at_measured_clock"] = round(achieved / at_clock, 4)
+        if "vendor_gemm_bf16_tflops" in counters:
+            line["roofline"]["frac_of_vendor_gemm"] = round(
+                achieved / counters["vendor_gemm_bf16_tflops"], 4)
     if "cpu" in head:
         line["cpu_baseline"] = head["cpu"]
         line["parity"] = head["parity"]
