@@ -49,11 +49,11 @@ constexpr int kKeyTile = 64;              // keys per staged K/V tile
 // The running maximum m is only raised when some p = 2^(s*c - m) of a tile
 // would exceed 2^kRescaleSlack.  Any stale maximum gives the same result: it
 // cancels between the numerator and the row sum.  The bound keeps every p,
-// and the fp32 sums over up to 2^31 keys, far from overflow, and makes a
-// raise rare once the first tile has set m.
-constexpr int kRescaleSlack = 32;
-constexpr float kRescaleBound = 4294967296.0f;   // 2^kRescaleSlack
-static_assert(kRescaleBound == (float)(1ull << kRescaleSlack), "bound mismatch");
+// and the fp32 sums over up to 2^31 keys of p times |v| < 2^30, below the
+// fp32 range, and makes a raise rare once the first tile has set m.
+constexpr int kRescaleSlack = 64;
+constexpr float kRescaleBound = 18446744073709551616.0f;   // 2^kRescaleSlack
+static_assert(kRescaleBound == 2.0f * (float)(1ull << 63), "bound mismatch");
 
 // LDS chunk swizzles (16-byte chunks of a D-wide bf16 row).  K is read as
 // 16-byte MFMA operands, one key row per lane; V is read with transposing
@@ -287,8 +287,11 @@ constexpr int phase_reads(int mode, int i) {
     return (mode == 1 || (mode == 0 && (i & 1) == 0)) ? 1 : 2;
 }
 
-// Row sums of P on the matrix cores (ones x P^T, four MFMAs per tile) instead
-// of 32 vector adds: for D < 128 the MFMA phase is the shorter one.
+// Every row sum adds the bf16-rounded p that the P V product uses, so the
+// weights of a row sum to one however sharply it peaks.  For D < 128 the
+// matrix cores form it (ones x P^T, four MFMAs per tile): there the MFMA
+// phase is the shorter one.  For D = 128 the vector phase adds the rounded
+// values in fp32.
 template <int D>
 constexpr bool kRowSumOnMfma = D < 128;
 
@@ -510,6 +513,16 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
         // 2^kRescaleSlack.  Tile 0 always takes the branch.
         f32x16 e0, e1;
         float ls[4];
+        // P to bf16, in the operand order of the P V MFMAs.
+        auto pack = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bf16x2 p0 = __builtin_convertvector((f32x2){e0[2 * e], e0[2 * e + 1]}, bf16x2);
+                const bf16x2 p1 = __builtin_convertvector((f32x2){e1[2 * e], e1[2 * e + 1]}, bf16x2);
+                pu[e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p0);
+                pu[2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
+            }
+        };
         auto sweep = [&](float m_sub) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -522,15 +535,18 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
                 e1[i] = __builtin_amdgcn_exp2f(e1[i]);
             }
             if constexpr (!kRowSumOnMfma<D>) {
-                // Row sums in fp32, four partial sums.  Plain adds: the bf16
-                // dot-product instruction would stall behind the partner
-                // wave's MFMAs.
+                // Row sums of the packed bf16 values in fp32, four partial
+                // sums.  Each half of a packed word is put back in place as
+                // an fp32; plain adds, since the bf16 dot-product instruction
+                // would stall behind the partner wave's MFMAs.
+                pack();
 #pragma unroll
-                for (int k = 0; k < 4; ++k) ls[k] = e0[k] + e1[k];
+                for (int k = 0; k < 4; ++k) ls[k] = 0.f;
 #pragma unroll
-                for (int i = 4; i < 16; ++i) {
-                    ls[i & 3] += e0[i];
-                    ls[i & 3] += e1[i];
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t w = pu[e >> 2][e & 3];
+                    ls[e & 3] += __builtin_bit_cast(float, w << 16);
+                    ls[e & 3] += __builtin_bit_cast(float, w & 0xffff0000u);
                 }
             }
         };
@@ -569,13 +585,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) l_run[k] += ls[k];
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const bf16x2 p0 = __builtin_convertvector((f32x2){e0[2 * e], e0[2 * e + 1]}, bf16x2);
-            const bf16x2 p1 = __builtin_convertvector((f32x2){e1[2 * e], e1[2 * e + 1]}, bf16x2);
-            pu[e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p0);
-            pu[2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
-        }
+        if constexpr (kRowSumOnMfma<D>) pack();
     };
     // Iteration t of every wave: the MFMA phase of tile t (S(t) from K(t), and
     // P(t-1) V(t-1)), a barrier, the vector phase of tile t, a barrier.  Tile j

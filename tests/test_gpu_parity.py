@@ -117,20 +117,39 @@ def test_aligned_shapes_bf16(B, Hq, Hkv, T, D, causal):
     full_case(B, Hq, Hkv, T, D, "bf16", causal, seed=T + 1)
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_scores_growing_along_the_keys(D):
+@pytest.mark.parametrize("D,rate,seed", [(64, 8.0, 5), (128, 8.0, 5), (128, 10.0, 7), (32, 10.0, 7)])
+def test_scores_growing_along_the_keys(D, rate, seed):
     """Key rows grow with position, so later tiles beat the running max by far
-    more than the lazy-rescale bound: the rescale path runs mid-sequence."""
+    more than the lazy-rescale bound: the rescale path runs mid-sequence.  The
+    late rows attend almost entirely to one key, which is where a row sum of
+    unrounded p against a P V product of rounded p would show."""
     B, Hq, Hkv, T = 1, 8, 2, 512
-    q, k, v = inputs.make_qkv(B, Hq, Hkv, T, D, "bf16", seed=5)
-    grow = (1.0 + torch.arange(T, dtype=torch.float32) / 8.0).view(1, 1, T, 1)
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, T, D, "bf16", seed=seed)
+    grow = (1.0 + torch.arange(T, dtype=torch.float32) / rate).view(1, 1, T, 1)
     k = (k.float() * grow).to(torch.bfloat16)
     scale = inputs.default_scale(D)
-    say(f"case growing keys B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
+    say(f"case growing keys B={B} Hq={Hq} Hkv={Hkv} T={T} D={D} rate={rate} seed={seed}")
     o, l = run_gpu(q, k, v, True, scale)
     O_ref, l_ref = oracle.attn_fwd(inputs.bits(q), inputs.bits(k), inputs.bits(v), True, scale)
     check_close(o, l, O_ref, l_ref, "bf16")
     assert l_ref.max() - l_ref.min() > 64 * math.log(2)   # the spread that forces rescales
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D,causal", [(32, True), (64, False), (128, True)])
+def test_identical_value_rows(dtype, D, causal):
+    """With every V row of a head equal, each output row is that row: the
+    softmax weights sum to one (for bf16 exactly the rounded weights the P V
+    product uses, so O comes back bit for bit)."""
+    B, Hq, Hkv, T = 2, 8, 2, 333
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, T, D, dtype, seed=D + 1)
+    v = v[:, :, :1, :].expand(B, Hkv, T, D).contiguous()
+    say(f"case identical V rows B={B} Hq={Hq} Hkv={Hkv} T={T} D={D} {dtype} causal={causal}")
+    o, _ = run_gpu(q, k, v, causal, inputs.default_scale(D))
+    want = np.repeat(v[:, :, :1, :].float().numpy().astype(np.float64), Hq // Hkv, axis=1)
+    err = np.abs(o - want).max()
+    say(f"max |O - v0| {err:.3e}")
+    assert err == 0.0 if dtype == "bf16" else err <= F32_MAX
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,D,causal", [
