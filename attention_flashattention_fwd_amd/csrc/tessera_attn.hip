@@ -52,8 +52,6 @@ constexpr int kKeyTile = 64;              // keys per staged K/V tile
 // and the fp32 sums over up to 2^31 keys of p times |v| < 2^30, below the
 // fp32 range, and makes a raise rare once the first tile has set m.
 constexpr int kRescaleSlack = 64;
-constexpr float kRescaleBound = 18446744073709551616.0f;   // 2^kRescaleSlack
-static_assert(kRescaleBound == 2.0f * (float)(1ull << 63), "bound mismatch");
 
 // LDS chunk swizzles (16-byte chunks of a D-wide bf16 row).  K is read as
 // 16-byte MFMA operands, one key row per lane; V is read with transposing
@@ -87,6 +85,9 @@ struct Bf16Args {
     float c;      // |scale| * log2(e)  (1 when scale == 0)
 };
 
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -220,12 +221,11 @@ __device__ __forceinline__ void phase_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Pins a vector phase's results to the end of that phase.  P and the row sum
-// feed only later code, so without this the compiler may sink their exp2 and
-// convert work past the barrier into the wave's own MFMA phase.
-__device__ __forceinline__ void settle(const u32x4 (&pu)[4], const float (&l)[4]) {
-    asm volatile("" ::"v"(pu[0]), "v"(pu[1]), "v"(pu[2]), "v"(pu[3]), "v"(l[0]), "v"(l[1]),
-                 "v"(l[2]), "v"(l[3]));
+// Pins a vector phase's result to the end of that phase.  P feeds only later
+// code, so without this the compiler may sink its exp2 and convert work past
+// the barrier into the wave's own MFMA phase.
+__device__ __forceinline__ void settle(const u32x4 (&pu)[4]) {
+    asm volatile("" ::"v"(pu[0]), "v"(pu[1]), "v"(pu[2]), "v"(pu[3]));
 }
 
 // max(x, x of lane l ^ 32): a swap of the wave's halves, without LDS.
@@ -287,13 +287,20 @@ constexpr int phase_reads(int mode, int i) {
     return (mode == 1 || (mode == 0 && (i & 1) == 0)) ? 1 : 2;
 }
 
-// Every row sum adds the bf16-rounded p that the P V product uses, so the
-// weights of a row sum to one however sharply it peaks.  For D < 128 the
-// matrix cores form it (ones x P^T, four MFMAs per tile): there the MFMA
-// phase is the shorter one.  For D = 128 the vector phase adds the rounded
-// values in fp32.
-template <int D>
-constexpr bool kRowSumOnMfma = D < 128;
+// Row sums on the matrix cores, from the same bf16 P that the P V product
+// uses, so the weights of a row sum to one however sharply it peaks.  One
+// 16x16x32 MFMA per 16-key step takes the P^T operand of the P V MFMAs as its
+// B operand.  Read that way, column n of B holds the keys of query n in lane
+// groups 0 and 2 and those of query n + 16 in lane groups 1 and 3, so an A
+// operand that is one on (row r, lane group g) with r + g even, else zero,
+// puts the sum of query n in the even rows of output column n and that of
+// query n + 16 in the odd rows.  Each lane then holds both in its entries 0
+// and 1 and keeps the one of its own query, (lane / 16) % 2.  Half the cost
+// of a 32x32 ones x P^T product, and no vector adds.
+__device__ __forceinline__ bf16x8 row_sum_selector(int lane) {
+    const __bf16 x = ((lane ^ (lane >> 4)) & 1) == 0 ? (__bf16)1.0f : (__bf16)0.0f;
+    return bf16x8{x, x, x, x, x, x, x, x};
+}
 
 
 // Scheduling groups for the MFMA phase: the row-sum MFMAs first (they need no
@@ -354,7 +361,7 @@ template <int D, int MODE, class Loads>
 __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, uint32_t vrel,
                                            const LaneOffsets<D> &off, const bf16x8 *qf,
                                            const u32x4 *pu, f32x16 &s0, f32x16 &s1, f32x16 *acc,
-                                           f32x16 &lsum, const Loads &loads,
+                                           f32x4 &lsum, bf16x8 sumsel, const Loads &loads,
                                            u32x4 (&ring)[kPrefetch]) {
     constexpr int kHalf = D / 8;                         // MFMAs of each kind
     constexpr int kN = MODE == 0 ? 2 * kHalf : kHalf;    // MFMAs in this phase
@@ -363,12 +370,11 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, uint32_t vrel,
         s0 = f32x16{};
         s1 = f32x16{};
     }
-    constexpr bool kSum = kRowSumOnMfma<D> && MODE != 1;
+    constexpr bool kSum = MODE != 1;
     if constexpr (kSum) {
-        const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
-                             (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) lsum = mfma32(ones, __builtin_bit_cast(bf16x8, pu[st]), lsum);
+        for (int st = 0; st < 4; ++st)
+            lsum = mfma16(sumsel, __builtin_bit_cast(bf16x8, pu[st]), lsum);
     }
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
@@ -476,8 +482,8 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
     float m_run = -INFINITY;   // running max of scale*log2(e)*s (log2 units)
-    float l_run[4] = {0.f, 0.f, 0.f, 0.f};   // this lane's share of the row sum, 4 parts
-    f32x16 lsum = f32x16{};   // row sums from the matrix cores (every entry the full sum)
+    f32x4 lsum = f32x4{};   // row sums: entry (lane / 16) % 2 is this lane's query
+    const bf16x8 sumsel = row_sum_selector(lane);
     const float c = a.c;
     f32x16 s0 = f32x16{}, s1 = f32x16{};   // scores of the tile in flight
     u32x4 pu[4];                           // its probabilities, bf16, per 16-key step
@@ -505,24 +511,12 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
         // Online softmax, in log2 units, with a lazy running max m.  P =
         // 2^(s*c - m) is computed with the current m before the tile has been
         // looked at; m only has to move when some p of the tile would exceed
-        // 2^kRescaleSlack.  The lane tests that on its own row sum when it
-        // forms one (D = 128), else on its own tile max.  Any lane that asks
-        // for a move makes the whole wave take the branch, which takes the
-        // tile max over both lanes of each query row (so both keep the same
-        // m), rescales the accumulators and recomputes P.  Every p is at most
-        // 2^kRescaleSlack.  Tile 0 always takes the branch.
+        // 2^kRescaleSlack, which the lane tests on its own tile max.  Any lane
+        // that asks for a move makes the whole wave take the branch, which
+        // takes the tile max over both lanes of each query row (so both keep
+        // the same m), rescales the accumulators and recomputes P.  Every p is
+        // at most 2^kRescaleSlack.  Tile 0 always takes the branch.
         f32x16 e0, e1;
-        float ls[4];
-        // P to bf16, in the operand order of the P V MFMAs.
-        auto pack = [&]() __attribute__((always_inline)) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const bf16x2 p0 = __builtin_convertvector((f32x2){e0[2 * e], e0[2 * e + 1]}, bf16x2);
-                const bf16x2 p1 = __builtin_convertvector((f32x2){e1[2 * e], e1[2 * e + 1]}, bf16x2);
-                pu[e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p0);
-                pu[2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
-            }
-        };
         auto sweep = [&](float m_sub) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -533,21 +527,6 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
             for (int i = 0; i < 16; ++i) {
                 e0[i] = __builtin_amdgcn_exp2f(e0[i]);
                 e1[i] = __builtin_amdgcn_exp2f(e1[i]);
-            }
-            if constexpr (!kRowSumOnMfma<D>) {
-                // Row sums of the packed bf16 values in fp32, four partial
-                // sums.  Each half of a packed word is put back in place as
-                // an fp32; plain adds, since the bf16 dot-product instruction
-                // would stall behind the partner wave's MFMAs.
-                pack();
-#pragma unroll
-                for (int k = 0; k < 4; ++k) ls[k] = 0.f;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const uint32_t w = pu[e >> 2][e & 3];
-                    ls[e & 3] += __builtin_bit_cast(float, w << 16);
-                    ls[e & 3] += __builtin_bit_cast(float, w & 0xffff0000u);
-                }
             }
         };
         auto own_max = [&]() __attribute__((always_inline)) {
@@ -562,30 +541,26 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
             }
             return fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])) * c;
         };
-        auto move_max = [&](float m_own) __attribute__((always_inline)) {
+        sweep(first ? 0.f : m_run);
+        const float m_own = own_max();
+        if (first || __builtin_amdgcn_ballot_w64(m_own > m_run + (float)kRescaleSlack) != 0) {
             const float m_new = fmaxf(m_run, max_with_partner(m_own));
             const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) l_run[k] *= alpha;
-            lsum[0] *= alpha;   // the only entry read
+            lsum[0] *= alpha;   // the two entries a lane may read
+            lsum[1] *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
             m_run = m_new;
             sweep(m_new == -INFINITY ? 0.f : m_new);
-        };
-        sweep(first ? 0.f : m_run);
-        if constexpr (kRowSumOnMfma<D>) {
-            const float m_own = own_max();
-            if (first || __builtin_amdgcn_ballot_w64(m_own > m_run + (float)kRescaleSlack) != 0)
-                move_max(m_own);
-        } else {
-            const float l_tile = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-            if (first || __builtin_amdgcn_ballot_w64(!(l_tile <= kRescaleBound)) != 0)
-                move_max(own_max());
-#pragma unroll
-            for (int k = 0; k < 4; ++k) l_run[k] += ls[k];
         }
-        if constexpr (kRowSumOnMfma<D>) pack();
+        // P to bf16, in the operand order of the P V MFMAs.
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bf16x2 p0 = __builtin_convertvector((f32x2){e0[2 * e], e0[2 * e + 1]}, bf16x2);
+            const bf16x2 p1 = __builtin_convertvector((f32x2){e1[2 * e], e1[2 * e + 1]}, bf16x2);
+            pu[e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p0);
+            pu[2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
+        }
     };
     // Iteration t of every wave: the MFMA phase of tile t (S(t) from K(t), and
     // P(t-1) V(t-1)), a barrier, the vector phase of tile t, a barrier.  Tile j
@@ -621,14 +596,14 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
         if (t + 1 < ntiles) preload<D, 0>(kbuf(kn), vn * kTB, off, ring);
         else preload<D, 2>(nullptr, vn * kTB, off, ring);
         softmax_phase(t, first);
-        settle(pu, l_run);
+        settle(pu);
         phase_barrier();
     };
     // Iteration t: K(t) in buffer kc, V(t-1) in vp; loads into kw, vw; the
     // next phase's K(t+1) in kn, V(t) in vn.
     auto iteration = [&](int t, int kc, int vp, int kw, int vw, int kn, int vn)
                          __attribute__((always_inline)) {
-        mfma_phase<D, 0>(kbuf(kc), vp * kTB, off, qf, pu, s0, s1, acc, lsum,
+        mfma_phase<D, 0>(kbuf(kc), vp * kTB, off, qf, pu, s0, s1, acc, lsum, sumsel,
                          loads(t, kbuf(kw), vbuf(vw)), ring);
         finish(t, kn, vn, false);
     };
@@ -639,7 +614,8 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     preload<D, 1>(kbuf(0), 0, off, ring);
     if (lag) phase_barrier();
     // Tile 0 has no P V yet.
-    mfma_phase<D, 1>(kbuf(0), 0, off, qf, pu, s0, s1, acc, lsum, loads(0, kbuf(3), vbuf(2)), ring);
+    mfma_phase<D, 1>(kbuf(0), 0, off, qf, pu, s0, s1, acc, lsum, sumsel,
+                     loads(0, kbuf(3), vbuf(2)), ring);
     finish(0, 1, 0, true);
     for (int t = 1; t < ntiles; t += 4) {
         iteration(t, 1, 0, 0, 3, 2, 1);
@@ -650,23 +626,20 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     // P V of the last tile, then the leading waves pass their extra barrier.
     const int last = (ntiles - 1) % 4;
     const NoLoads none;
-    if (last == 0) mfma_phase<D, 2>(nullptr, 0 * kTB, off, qf, pu, s0, s1, acc, lsum, none, ring);
-    else if (last == 1) mfma_phase<D, 2>(nullptr, 1 * kTB, off, qf, pu, s0, s1, acc, lsum, none, ring);
-    else if (last == 2) mfma_phase<D, 2>(nullptr, 2 * kTB, off, qf, pu, s0, s1, acc, lsum, none, ring);
-    else mfma_phase<D, 2>(nullptr, 3 * kTB, off, qf, pu, s0, s1, acc, lsum, none, ring);
+    auto pv_last = [&](uint32_t vrel) __attribute__((always_inline)) {
+        mfma_phase<D, 2>(nullptr, vrel, off, qf, pu, s0, s1, acc, lsum, sumsel, none, ring);
+    };
+    if (last == 0) pv_last(0 * kTB);
+    else if (last == 1) pv_last(1 * kTB);
+    else if (last == 2) pv_last(2 * kTB);
+    else pv_last(3 * kTB);
     if (!lag) phase_barrier();
     // The clamped loads of the last phases must land before the workgroup's
     // LDS is released.
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // Epilogue: O = acc / l, rounded once to bf16; lse = ln 2 * (m + log2 l).
-    float l_tot;
-    if constexpr (kRowSumOnMfma<D>) {
-        l_tot = lsum[0];
-    } else {
-        const float l_own = (l_run[0] + l_run[1]) + (l_run[2] + l_run[3]);
-        l_tot = l_own + __shfl_xor(l_own, 32);
-    }
+    const float l_tot = ((lane >> 4) & 1) ? lsum[1] : lsum[0];
     if (query < T) {
         const float inv = 1.f / l_tot;
         uint16_t *dst = a.o + (q_row0 + query) * D;
