@@ -46,6 +46,7 @@ constexpr double kLog2e = 1.442695040888963407;
 constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kKeyTile = 64;              // keys per staged K/V tile
+constexpr int kPairedMinGrid = 2048;      // D = 64 grids that run two workgroups per CU
 // The running maximum m is only raised when some p = 2^(s*c - m) of a tile
 // would exceed 2^kRescaleSlack.  Any stale maximum gives the same result: it
 // cancels between the numerator and the row sum.  The bound keeps every p,
@@ -226,6 +227,14 @@ __device__ __forceinline__ void phase_barrier() {
 // the barrier into the wave's own MFMA phase.
 __device__ __forceinline__ void settle(const u32x4 (&pu)[4]) {
     asm volatile("" ::"v"(pu[0]), "v"(pu[1]), "v"(pu[2]), "v"(pu[3]));
+}
+
+// The lane index, computed where it is called: the compiler cannot tie it to an
+// earlier copy and keep that one live instead.
+__device__ __forceinline__ int lane_id_opaque() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
 }
 
 // max(x, x of lane l ^ 32): a swap of the wave's halves, without LDS.
@@ -418,8 +427,17 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, uint32_t vrel,
 // the schedule of loads, waits and reads is spelled out at the loop below,
 // which is unrolled by four so every LDS buffer is a distinct array.
 // RAGGED: T % kKeyTile != 0 (the last key tile crosses T).
-template <int D, bool RAGGED>
-__global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
+// PAIRED: two workgroups per CU (four waves per SIMD, at most 128 VGPRs each;
+// D = 64 with T a multiple of the key tile only: the LDS ring is 64 KB, and
+// the ragged build would spill in the loop).  The two run independently, so the
+// vector phases of one overlap the matrix-core phases of the other on top of
+// the ping-pong inside each: the vector work of a single wave is bound by its
+// own issue rate, and two waves issuing it side by side go about twice as fast.
+template <int D, bool RAGGED, bool PAIRED>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(PAIRED ? 4 : 2)))
+attn_fwd_bf16_kernel(Bf16Args a) {
+    static_assert(!PAIRED || (D == 64 && !RAGGED), "two workgroups per CU: D = 64, T % 64 == 0");
     __shared__ LdsRing<D> lds;
 
     const int tid = threadIdx.x;
@@ -639,10 +657,15 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // Epilogue: O = acc / l, rounded once to bf16; lse = ln 2 * (m + log2 l).
-    const float l_tot = ((lane >> 4) & 1) ? lsum[1] : lsum[0];
-    if (query < T) {
+    // The lane index is read again here rather than kept across the loop,
+    // where registers are scarcest (two workgroups per CU allow 128).
+    const int lane_e = lane_id_opaque();
+    const int hi_e = lane_e >> 5;
+    const int query_e = qw0 + (lane_e & 31);
+    const float l_tot = ((lane_e >> 4) & 1) ? lsum[1] : lsum[0];
+    if (query_e < T) {
         const float inv = 1.f / l_tot;
-        uint16_t *dst = a.o + (q_row0 + query) * D;
+        uint16_t *dst = a.o + (q_row0 + query_e) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -651,10 +674,10 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g4 + e] * inv;
                 const bf16x4 y = __builtin_convertvector(x, bf16x4);
-                *(bf16x4 *)(dst + 32 * db + 8 * g4 + 4 * hi) = y;
+                *(bf16x4 *)(dst + 32 * db + 8 * g4 + 4 * hi_e) = y;
             }
         }
-        if (hi == 0) a.lse[q_row0 + query] = (m_run + log2f(l_tot)) * kLn2;
+        if (hi_e == 0) a.lse[q_row0 + query_e] = (m_run + log2f(l_tot)) * kLn2;
     }
 }
 
@@ -803,15 +826,21 @@ extern "C" int tessera_attn_fwd(const void *q, const void *k, const void *v, voi
     hipStream_t s = (hipStream_t)stream;
     const dim3 g((unsigned)grid), blk(kThreads);
     const bool ragged = T % kKeyTile != 0;
+    // Two workgroups per CU pay off once the grid covers the 512 slots of 256
+    // CUs several times over; on a grid that fills them about once, the pairs
+    // that land together are too uneven in length (causal tiles differ).
+    const bool paired = grid >= kPairedMinGrid && !ragged;
     if (D == 128) {
-        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), g, blk, 0, s, a);
+        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true, false>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false, false>), g, blk, 0, s, a);
+    } else if (D == 64 && paired) {
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false, true>), g, blk, 0, s, a);
     } else if (D == 64) {
-        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), g, blk, 0, s, a);
+        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true, false>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false, false>), g, blk, 0, s, a);
     } else {
-        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<32, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<32, false>), g, blk, 0, s, a);
+        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<32, true, false>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<32, false, false>), g, blk, 0, s, a);
     }
     return launch_status();
 }

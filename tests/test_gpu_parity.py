@@ -117,6 +117,22 @@ def test_aligned_shapes_bf16(B, Hq, Hkv, T, D, causal):
     full_case(B, Hq, Hkv, T, D, "bf16", causal, seed=T + 1)
 
 
+# D = 64 grids of 2048 or more workgroups (query tiles x B x Hkv) with T a
+# multiple of 64 run two workgroups per CU, a kernel build of their own; a
+# ragged T of that size takes the one-workgroup build.  Each is compared
+# element by element.
+PAIRED = [
+    (128, 32, 8, 128, 64, True),    # 2 query tiles x 1024 = 2048 workgroups
+    (128, 16, 16, 128, 64, False),  # MHA: 256-row tiles, 1 x 2048
+    (86, 32, 8, 130, 64, True),     # 3 x 688, ragged: one workgroup per CU
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D,causal", PAIRED)
+def test_two_workgroups_per_cu_shapes(B, Hq, Hkv, T, D, causal):
+    full_case(B, Hq, Hkv, T, D, "bf16", causal, seed=B + T)
+
+
 @pytest.mark.parametrize("D,rate,seed", [(64, 8.0, 5), (128, 8.0, 5), (128, 10.0, 7), (32, 10.0, 7)])
 def test_scores_growing_along_the_keys(D, rate, seed):
     """Key rows grow with position, so later tiles beat the running max by far
