@@ -12,7 +12,8 @@ Printed: ONE JSON line with the metric, a roofline object for the attention
 kernel (achieved from HIP events around the timed steps on the kernel's
 stream), the fp64 CPU oracle timed on a bounded sample of the same workload
 (the CPU baseline), a parity check of the timed output against that oracle
-sample, and the secondary workloads timed the same way.
+sample, and the secondary workloads timed the same way (each after at least
+0.2 s of warm-up launches, since they follow the CPU sample's idle spell).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -43,7 +44,7 @@ def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="wall-time budget of the CPU-oracle baseline sample")
@@ -87,25 +88,38 @@ def recorded_traffic():
     return float(m_b.group(1)), extra
 
 
-def time_steps(torch, fn, steps, warmup, stream):
-    """W untimed steps, then K timed steps bracketed by synchronisation.  HIP
-    events on the kernel's stream sit between consecutive launches, so besides
-    the mean GPU time of the K steps the per-launch median and minimum come
-    out of the same run."""
+def time_steps(torch, fn, steps, warmup, stream, warm_seconds=0.0):
+    """W untimed steps (continued until warm_seconds of wall time have passed:
+    after an idle spell the shader clock takes tens of milliseconds of load to
+    settle), then K timed steps back to back, bracketed by synchronisation and
+    by two HIP events on the kernel's stream.  A second pass of K steps, with
+    an event between consecutive launches, gives the per-launch median and
+    minimum; it is not part of the timed region."""
     with torch.cuda.stream(stream):
-        for _ in range(warmup):
+        t_w = time.perf_counter()
+        n = 0
+        while n < warmup or time.perf_counter() - t_w < warm_seconds:
             fn()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()   # keep the host clock in step with the GPU
         torch.cuda.synchronize()
-        events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = start.elapsed_time(end) / steps
+        events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         events[0].record(stream)
         for i in range(steps):
             fn()
             events[i + 1].record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
     per = sorted(events[i].elapsed_time(events[i + 1]) for i in range(steps))
-    gpu_ms = events[0].elapsed_time(events[steps]) / steps
     return gpu_ms, wall * 1e3 / steps, per[len(per) // 2], per[0]
 
 
@@ -211,7 +225,7 @@ def main(argv=None):
                           "launches": max(1, args.steps) + args.warmup}))
         return 0
 
-    def measure(name, steps, warmup, with_cpu):
+    def measure(name, steps, warmup, with_cpu, warm_seconds=0.0):
         w = inputs.WORKLOADS[name]
         q, k, v = inputs.make_workload(w)
         qd, kd, vd = (t.to(dev) for t in (q, k, v))
@@ -220,7 +234,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         fn = lambda: binding.attn_fwd_into(qd, kd, vd, out, lse, w.causal, w.scale,  # noqa: E731
                                            stream=stream)
-        gpu_ms, wall_ms, med_ms, min_ms = time_steps(torch, fn, steps, warmup, stream)
+        gpu_ms, wall_ms, med_ms, min_ms = time_steps(torch, fn, steps, warmup, stream,
+                                                     warm_seconds)
         res = {"w": w, "gpu_ms": gpu_ms, "wall_ms": wall_ms, "med_ms": med_ms, "min_ms": min_ms}
         if with_cpu:
             res["cpu"], res["parity"] = cpu_baseline(w, q, k, v, out, lse, args.cpu_seconds)
@@ -237,7 +252,7 @@ def main(argv=None):
         for name in SECONDARY:
             if name == w.name:
                 continue
-            r = measure(name, max(5, args.steps // 2), args.warmup, False)
+            r = measure(name, max(5, args.steps // 2), args.warmup, False, warm_seconds=0.2)
             secondary[name] = {
                 "config": r["w"].describe(),
                 "us_per_call": round(r["gpu_ms"] * 1e3, 2),
