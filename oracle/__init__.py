@@ -6,6 +6,7 @@ import this package.  The HIP library never uses it.
 from .oracle import (  # noqa: F401
     OracleLib,
     attn_fwd,
+    attn_fwd_kv,
     attn_probs,
     attn_rows,
     build,

@@ -30,6 +30,15 @@
  *
  * A query row with no visible key (impossible for these shapes, since key i
  * is always visible to query i) would get O = 0 and lse = -inf.
+ *
+ * Continuation of a cached sequence (tessera_oracle_attn_fwd_kv).  The same
+ * page, section "Serving: block-paged KV, batch recomposition, speculation",
+ * holds that decoding incrementally with the KV cache gives what a full
+ * forward pass gives.  With Tq query rows against Tk key rows, query row i
+ * stands at sequence position i + Tk - Tq, so the causal key set becomes
+ * J = { j : 0 <= j <= i + Tk - Tq } (all Tk keys when not causal); q and O
+ * are [B,Hq,Tq,D], k and v [B,Hkv,Tk,D], lse [B,Hq,Tq].  Tq = Tk = T is the
+ * definition above.  A causal row with i + Tk - Tq < 0 has no visible key.
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,31 +63,33 @@ static double widen(const void *p, int dtype, int64_t idx)
 }
 
 static int check_args(const void *q, const void *k, const void *v, int dtype,
-                      int B, int Hq, int Hkv, int T, int D, int causal)
+                      int B, int Hq, int Hkv, int Tq, int Tk, int D, int causal)
 {
     if (!q || !k || !v) return 1;
     if (dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16) return 2;
-    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || D < 1) return 3;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || Tk < 1 || D < 1) return 3;
     if (Hq % Hkv != 0) return 4;
     if (causal != 0 && causal != 1) return 5;
     return 0;
 }
 
 /*
- * One query row.  `s` is caller scratch of T doubles, `p` of T doubles.
- * Writes D values to `o` and one to `lse`; if `probs` is not NULL it also
- * writes the T softmax weights of the row (0 for masked keys).
+ * One query row of Tq against Tk keys.  `s` and `p` are caller scratch of Tk
+ * doubles each.  Writes D values to `o` and one to `lse`; if `probs` is not
+ * NULL it also writes the Tk softmax weights of the row (0 for masked keys).
  */
 static void one_row(const void *q, const void *k, const void *v, int dtype,
-                    int Hq, int Hkv, int T, int D, int causal, double scale,
+                    int Hq, int Hkv, int Tq, int Tk, int D, int causal, double scale,
                     int b, int h, int i, double *s, double *p, double *o,
                     double *lse, double *probs)
 {
     const int G = Hq / Hkv;
     const int g = h / G;
-    const int64_t qrow = (((int64_t)b * Hq + h) * T + i) * D;
-    const int64_t kv0 = ((int64_t)b * Hkv + g) * T * D;
-    const int n = causal ? i + 1 : T; /* visible keys are 0 .. n-1 */
+    const int64_t qrow = (((int64_t)b * Hq + h) * Tq + i) * D;
+    const int64_t kv0 = ((int64_t)b * Hkv + g) * Tk * D;
+    const int pos = i + (Tk - Tq);          /* sequence position of query row i */
+    int n = causal ? pos + 1 : Tk;          /* visible keys are 0 .. n-1 */
+    if (n < 0) n = 0;
 
     /* pass 1: scaled scores and their maximum */
     double m = -INFINITY;
@@ -93,7 +104,7 @@ static void one_row(const void *q, const void *k, const void *v, int dtype,
     for (int d = 0; d < D; ++d) o[d] = 0.0;
     if (n == 0) { /* no visible key */
         *lse = -INFINITY;
-        if (probs) for (int j = 0; j < T; ++j) probs[j] = 0.0;
+        if (probs) for (int j = 0; j < Tk; ++j) probs[j] = 0.0;
         return;
     }
 
@@ -111,7 +122,7 @@ static void one_row(const void *q, const void *k, const void *v, int dtype,
     *lse = m + log(Z);
 
     if (probs) {
-        for (int j = 0; j < T; ++j) probs[j] = (j < n) ? p[j] / Z : 0.0;
+        for (int j = 0; j < Tk; ++j) probs[j] = (j < n) ? p[j] / Z : 0.0;
     }
 }
 
@@ -135,7 +146,7 @@ int tessera_oracle_attn_rows(const void *q, const void *k, const void *v, int dt
                              double scale, const int64_t *rows, int64_t nrows,
                              double *O, double *lse, int nthreads)
 {
-    int rc = check_args(q, k, v, dtype, B, Hq, Hkv, T, D, causal);
+    int rc = check_args(q, k, v, dtype, B, Hq, Hkv, T, T, D, causal);
     if (rc) return rc;
     if (nrows < 0 || (nrows > 0 && (!rows || !O || !lse))) return 6;
     const int64_t total = (int64_t)B * Hq * T;
@@ -158,8 +169,43 @@ int tessera_oracle_attn_rows(const void *q, const void *k, const void *v, int dt
                 const int64_t bh = flat / T;
                 const int h = (int)(bh % Hq);
                 const int b = (int)(bh / Hq);
-                one_row(q, k, v, dtype, Hq, Hkv, T, D, causal, scale, b, h, i, s, p,
+                one_row(q, k, v, dtype, Hq, Hkv, T, T, D, causal, scale, b, h, i, s, p,
                         O + r * D, lse + r, NULL);
+            }
+        }
+        free(s);
+        free(p);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Tq query rows against Tk key rows: O [B,Hq,Tq,D], lse [B,Hq,Tq]. */
+int tessera_oracle_attn_fwd_kv(const void *q, const void *k, const void *v, int dtype,
+                               int B, int Hq, int Hkv, int Tq, int Tk, int D, int causal,
+                               double scale, double *O, double *lse, int nthreads)
+{
+    int rc = check_args(q, k, v, dtype, B, Hq, Hkv, Tq, Tk, D, causal);
+    if (rc) return rc;
+    if (!O || !lse) return 6;
+    const int64_t total = (int64_t)B * Hq * Tq;
+
+    int failed = 0;
+    const int nt = resolve_threads(nthreads);
+#pragma omp parallel num_threads(nt) reduction(| : failed)
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)Tk);
+        double *p = (double *)malloc(sizeof(double) * (size_t)Tk);
+        if (!s || !p) {
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t flat = 0; flat < total; ++flat) {
+                const int i = (int)(flat % Tq);
+                const int64_t bh = flat / Tq;
+                const int h = (int)(bh % Hq);
+                const int b = (int)(bh / Hq);
+                one_row(q, k, v, dtype, Hq, Hkv, Tq, Tk, D, causal, scale, b, h, i, s, p,
+                        O + flat * D, lse + flat, NULL);
             }
         }
         free(s);
@@ -173,34 +219,8 @@ int tessera_oracle_attn_fwd(const void *q, const void *k, const void *v, int dty
                             int B, int Hq, int Hkv, int T, int D, int causal,
                             double scale, double *O, double *lse, int nthreads)
 {
-    int rc = check_args(q, k, v, dtype, B, Hq, Hkv, T, D, causal);
-    if (rc) return rc;
-    if (!O || !lse) return 6;
-    const int64_t total = (int64_t)B * Hq * T;
-
-    int failed = 0;
-    const int nt = resolve_threads(nthreads);
-#pragma omp parallel num_threads(nt) reduction(| : failed)
-    {
-        double *s = (double *)malloc(sizeof(double) * (size_t)T);
-        double *p = (double *)malloc(sizeof(double) * (size_t)T);
-        if (!s || !p) {
-            failed = 1;
-        } else {
-#pragma omp for schedule(dynamic, 4)
-            for (int64_t flat = 0; flat < total; ++flat) {
-                const int i = (int)(flat % T);
-                const int64_t bh = flat / T;
-                const int h = (int)(bh % Hq);
-                const int b = (int)(bh / Hq);
-                one_row(q, k, v, dtype, Hq, Hkv, T, D, causal, scale, b, h, i, s, p,
-                        O + flat * D, lse + flat, NULL);
-            }
-        }
-        free(s);
-        free(p);
-    }
-    return failed ? -1 : 0;
+    return tessera_oracle_attn_fwd_kv(q, k, v, dtype, B, Hq, Hkv, T, T, D, causal, scale,
+                                      O, lse, nthreads);
 }
 
 /* Attention plus the softmax weights P [B,Hq,T,T] (masked keys get 0). */
@@ -208,7 +228,7 @@ int tessera_oracle_attn_probs(const void *q, const void *k, const void *v, int d
                               int B, int Hq, int Hkv, int T, int D, int causal,
                               double scale, double *O, double *lse, double *P)
 {
-    int rc = check_args(q, k, v, dtype, B, Hq, Hkv, T, D, causal);
+    int rc = check_args(q, k, v, dtype, B, Hq, Hkv, T, T, D, causal);
     if (rc) return rc;
     if (!O || !lse || !P) return 6;
     double *s = (double *)malloc(sizeof(double) * (size_t)T);
@@ -224,7 +244,7 @@ int tessera_oracle_attn_probs(const void *q, const void *k, const void *v, int d
         const int64_t bh = flat / T;
         const int h = (int)(bh % Hq);
         const int b = (int)(bh / Hq);
-        one_row(q, k, v, dtype, Hq, Hkv, T, D, causal, scale, b, h, i, s, p,
+        one_row(q, k, v, dtype, Hq, Hkv, T, T, D, causal, scale, b, h, i, s, p,
                 O + flat * D, lse + flat, P + flat * T);
     }
     free(s);

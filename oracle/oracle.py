@@ -47,6 +47,9 @@ class OracleLib:
                   ctypes.c_int, ctypes.c_double]
         lib.tessera_oracle_attn_fwd.argtypes = common + [_c_double_p, _c_double_p, ctypes.c_int]
         lib.tessera_oracle_attn_fwd.restype = ctypes.c_int
+        lib.tessera_oracle_attn_fwd_kv.argtypes = common[:7] + [ctypes.c_int] + common[7:] + [
+            _c_double_p, _c_double_p, ctypes.c_int]
+        lib.tessera_oracle_attn_fwd_kv.restype = ctypes.c_int
         lib.tessera_oracle_attn_rows.argtypes = common + [
             _c_int64_p, ctypes.c_int64, _c_double_p, _c_double_p, ctypes.c_int]
         lib.tessera_oracle_attn_rows.restype = ctypes.c_int
@@ -58,7 +61,7 @@ class OracleLib:
 
     # -- helpers -----------------------------------------------------------
     @staticmethod
-    def _prep(q, k, v):
+    def _prep(q, k, v, same_rows=True):
         arrs = [np.ascontiguousarray(a) for a in (q, k, v)]
         dt = arrs[0].dtype
         if any(a.dtype != dt for a in arrs):
@@ -73,7 +76,7 @@ class OracleLib:
             raise ValueError("q, k, v must be 4-D [B, H, T, D]")
         B, Hq, T, D = arrs[0].shape
         if arrs[1].shape != arrs[2].shape or arrs[1].shape[0] != B or \
-                arrs[1].shape[2] != T or arrs[1].shape[3] != D:
+                (same_rows and arrs[1].shape[2] != T) or arrs[1].shape[3] != D:
             raise ValueError("k and v must be [B, Hkv, T, D] matching q")
         Hkv = arrs[1].shape[1]
         return arrs, code, (B, Hq, Hkv, T, D)
@@ -97,6 +100,20 @@ class OracleLib:
             int(bool(causal)), float(scale),
             O.ctypes.data_as(_c_double_p), lse.ctypes.data_as(_c_double_p), int(nthreads))
         self._check(rc, "tessera_oracle_attn_fwd")
+        return O, lse
+
+    def attn_fwd_kv(self, q, k, v, causal: bool, scale: float, nthreads: int = 0):
+        """q [B,Hq,Tq,D] against k, v [B,Hkv,Tk,D]; query row i stands at position
+        i + Tk - Tq.  Returns O [B,Hq,Tq,D], lse [B,Hq,Tq]."""
+        (q, k, v), code, (B, Hq, Hkv, Tq, D) = self._prep(q, k, v, same_rows=False)
+        Tk = k.shape[2]
+        O = np.empty((B, Hq, Tq, D), np.float64)
+        lse = np.empty((B, Hq, Tq), np.float64)
+        rc = self.lib.tessera_oracle_attn_fwd_kv(
+            self._ptr(q), self._ptr(k), self._ptr(v), code, B, Hq, Hkv, Tq, Tk, D,
+            int(bool(causal)), float(scale),
+            O.ctypes.data_as(_c_double_p), lse.ctypes.data_as(_c_double_p), int(nthreads))
+        self._check(rc, "tessera_oracle_attn_fwd_kv")
         return O, lse
 
     def attn_rows(self, q, k, v, causal: bool, scale: float, rows, nthreads: int = 0):
@@ -144,6 +161,10 @@ def load() -> OracleLib:
 
 def attn_fwd(q, k, v, causal, scale, nthreads=0):
     return load().attn_fwd(q, k, v, causal, scale, nthreads)
+
+
+def attn_fwd_kv(q, k, v, causal, scale, nthreads=0):
+    return load().attn_fwd_kv(q, k, v, causal, scale, nthreads)
 
 
 def attn_rows(q, k, v, causal, scale, rows, nthreads=0):

@@ -112,10 +112,12 @@ def pin_golden(lib):
 # brute force in 50-digit arithmetic on tiny inputs
 # ---------------------------------------------------------------------------
 def mp_attention(qv, kv, vv, causal, scale):
-    """Softmax attention by brute force with mpmath (no max subtraction)."""
+    """Softmax attention by brute force with mpmath (no max subtraction).  With
+    Tq query rows and Tk key rows, query row i is at sequence position
+    i + Tk - Tq and, under the causal mask, sees keys 0 .. i + Tk - Tq."""
     mpmath.mp.dps = 50
     B, Hq, T, D = qv.shape
-    Hkv = kv.shape[1]
+    Hkv, Tk = kv.shape[1], kv.shape[2]
     G = Hq // Hkv
     O = np.zeros((B, Hq, T, D))
     lse = np.zeros((B, Hq, T))
@@ -124,7 +126,7 @@ def mp_attention(qv, kv, vv, causal, scale):
         for h in range(Hq):
             kvh = h // G
             for i in range(T):
-                keys = range(i + 1) if causal else range(T)
+                keys = range(i + (Tk - T) + 1) if causal else range(Tk)
                 e = []
                 for j in keys:
                     dot = mpmath.fsum(mpmath.mpf(qv[b, h, i, d]) * mpmath.mpf(kv[b, kvh, j, d])
@@ -314,6 +316,63 @@ def pin_key_permutation(lib):
     assert not np.allclose(O3, O4)
 
 
+# ---------------------------------------------------------------------------
+# continuation of a cached sequence: Tq query rows against Tk key rows
+# ---------------------------------------------------------------------------
+def rand_kv_inputs(B, Hq, Hkv, Tq, Tk, D, dtype, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, Tq, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, Tk, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, Tk, D)).astype(np.float32)
+    return tuple(as_dtype(a, dtype) for a in (q, k, v))
+
+
+def pin_kv_mpmath(lib):
+    """Brute force at 50 digits with the causal mask aligned to the last key."""
+    cases = [(1, 2, 1, 1, 5, 3, True), (2, 4, 2, 3, 8, 4, True), (1, 3, 3, 6, 6, 2, True),
+             (2, 4, 1, 2, 7, 4, False), (1, 2, 1, 5, 3, 2, False)]
+    for n, (B, Hq, Hkv, Tq, Tk, D, causal) in enumerate(cases):
+        for dtype in ("fp32", "bf16"):
+            q, k, v = rand_kv_inputs(B, Hq, Hkv, Tq, Tk, D, dtype, seed=400 + n)
+            scale = fp32(0.6 + 0.1 * n)
+            O, lse = lib.attn_fwd_kv(q, k, v, causal, scale)
+            Om, lm = mp_attention(values(q), values(k), values(v), causal, scale)
+            assert np.abs(O - Om).max() <= 1e-12, (B, Hq, Hkv, Tq, Tk, D, dtype, causal)
+            assert np.abs(lse - lm).max() <= 1e-12, (B, Hq, Hkv, Tq, Tk, D, dtype, causal)
+
+
+def pin_kv_suffix_of_full_forward(lib):
+    """The pages' serving invariant: the last Tq rows of a full forward over T
+    positions equal Tq new rows computed against the cached T keys."""
+    B, Hq, Hkv, T, D = 2, 4, 2, 29, 8
+    q, k, v = rand_inputs(B, Hq, Hkv, T, D, "bf16", seed=17)
+    for causal in (True, False):
+        O, lse = lib.attn_fwd(q, k, v, causal, 0.3)
+        for Tq in (1, 2, 13, T):
+            Ok, lk = lib.attn_fwd_kv(np.ascontiguousarray(q[:, :, T - Tq:]), k, v, causal, 0.3)
+            assert np.array_equal(Ok, O[:, :, T - Tq:]), (causal, Tq)
+            assert np.array_equal(lk, lse[:, :, T - Tq:]), (causal, Tq)
+
+
+def pin_kv_torch_sdpa(lib):
+    """torch SDPA in float64 with an explicit mask: key j visible to query row
+    i iff j <= i + Tk - Tq."""
+    for n, (B, Hq, Hkv, Tq, Tk, D) in enumerate([(2, 6, 2, 9, 40, 16), (1, 4, 4, 33, 33, 8),
+                                                (1, 8, 1, 1, 70, 32)]):
+        q, k, v = rand_kv_inputs(B, Hq, Hkv, Tq, Tk, D, "bf16", seed=500 + n)
+        scale = fp32(1.0 / math.sqrt(D))
+        qt, kt, vt = (torch.from_numpy(values(a)) for a in (q, k, v))
+        kt = kt.repeat_interleave(Hq // Hkv, dim=1)
+        vt = vt.repeat_interleave(Hq // Hkv, dim=1)
+        visible = torch.arange(Tk)[None, :] <= torch.arange(Tq)[:, None] + (Tk - Tq)
+        O, lse = lib.attn_fwd_kv(q, k, v, True, scale)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=visible,
+                                                               scale=scale)
+        assert np.abs(O - ref.numpy()).max() <= 1e-12, (B, Hq, Hkv, Tq, Tk, D)
+        s = ((qt @ kt.transpose(-1, -2)) * scale).masked_fill(~visible, float("-inf"))
+        assert np.abs(lse - torch.logsumexp(s, dim=-1).numpy()).max() <= 1e-12
+
+
 def pin_rows_entry(lib):
     """The sampled-rows entry returns exactly the rows of the full call."""
     B, Hq, Hkv, T, D = 2, 4, 2, 33, 16
@@ -329,4 +388,5 @@ def pin_rows_entry(lib):
 ALL_PINS = [pin_golden, pin_mpmath, pin_torch_sdpa, pin_weights_sum_to_one, pin_probs_export,
             pin_causal_row0, pin_identical_value_rows, pin_uniform_scores,
             pin_gqa_equals_repeated_mha, pin_lse_closed_form, pin_key_shift,
-            pin_key_permutation, pin_rows_entry]
+            pin_key_permutation, pin_rows_entry, pin_kv_mpmath, pin_kv_suffix_of_full_forward,
+            pin_kv_torch_sdpa]

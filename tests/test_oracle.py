@@ -29,9 +29,13 @@ def test_pin(lib, pin):
 # pins leave that part of the oracle unchecked.
 MUTANTS = {
     "interleaved_head_map": ("const int g = h / G;", "const int g = h % Hkv;"),
-    "mask_hides_diagonal": ("causal ? i + 1 : T", "causal ? i : T"),
-    "mask_leaks_next_key": ("causal ? i + 1 : T", "causal ? (i + 2 < T ? i + 2 : T) : T"),
-    "mask_ignored": ("causal ? i + 1 : T", "T"),
+    "mask_hides_diagonal": ("causal ? pos + 1 : Tk", "causal ? pos : Tk"),
+    "mask_leaks_next_key": ("causal ? pos + 1 : Tk", "causal ? (pos + 2 < Tk ? pos + 2 : Tk) : Tk"),
+    "mask_ignored": ("causal ? pos + 1 : Tk", "Tk"),
+    "cache_offset_dropped": ("const int pos = i + (Tk - Tq);", "const int pos = i;"),
+    "cache_offset_reversed": ("const int pos = i + (Tk - Tq);", "const int pos = i + (Tq - Tk);"),
+    "key_stride_from_queries": ("* Tk * D;", "* Tq * D;"),
+    "query_stride_from_keys": ("* Tq + i) * D;", "* Tk + i) * D;"),
     "scale_dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
     "scale_squared": ("s[j] = scale * dot;", "s[j] = scale * scale * dot;"),
     "lse_without_max": ("*lse = m + log(Z);", "*lse = log(Z);"),
@@ -43,7 +47,7 @@ MUTANTS = {
     "dropped_last_dim": ("for (int d = 0; d < D; ++d)\n            dot +=",
                          "for (int d = 0; d < D - 1; ++d)\n            dot +="),
     "bf16_widen_shift": ("<< 16;", "<< 15;"),
-    "query_row_stride": ("* T + i) * D;", "* T + i) * D + (i > 0);"),
+    "query_row_stride": ("* Tq + i) * D;", "* Tq + i) * D + (i > 0);"),
     "value_from_query_head": ("o[d] += w * widen(v, dtype, kv0 +",
                               "o[d] += w * widen(v, dtype, (int64_t)0 * kv0 +"),
 }
