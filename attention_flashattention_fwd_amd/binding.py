@@ -28,8 +28,8 @@ ERR_ALIAS = 7
 ERR_TOO_LARGE = 8
 ERR_LAUNCH = 9
 
-EXPORTS = ("tessera_attn_fwd", "tessera_attn_fwd_f32", "tessera_attn_status_string",
-           "tessera_attn_last_error", "tessera_attn_version")
+EXPORTS = ("tessera_attn_fwd", "tessera_attn_fwd_kv", "tessera_attn_fwd_f32",
+           "tessera_attn_status_string", "tessera_attn_last_error", "tessera_attn_version")
 
 _lib = None
 
@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.tessera_attn_fwd.restype = i
         L.tessera_attn_fwd_f32.argtypes = sig
         L.tessera_attn_fwd_f32.restype = i
+        L.tessera_attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        L.tessera_attn_fwd_kv.restype = i
         L.tessera_attn_status_string.argtypes = [i]
         L.tessera_attn_status_string.restype = ctypes.c_char_p
         L.tessera_attn_last_error.argtypes = []
@@ -78,7 +80,14 @@ def raw_fwd(dtype: str, q, k, v, out, lse, B, Hq, Hkv, T, D, causal, scale, stre
                   float(np.float32(scale)), stream))
 
 
-def _check_inputs(q, k, v):
+def raw_fwd_kv(q, k, v, out, lse, B, Hq, Hkv, Tq, Tk, D, causal, scale, stream) -> int:
+    """Call tessera_attn_fwd_kv (bf16) with integer device addresses; returns the status."""
+    return int(lib().tessera_attn_fwd_kv(q, k, v, out, lse, int(B), int(Hq), int(Hkv), int(Tq),
+                                         int(Tk), int(D), int(causal),
+                                         float(np.float32(scale)), stream))
+
+
+def _check_inputs(q, k, v, same_rows: bool = True):
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -95,9 +104,12 @@ def _check_inputs(q, k, v):
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
     B, Hq, T, D = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != T or k.shape[3] != D:
-        raise ValueError(f"k, v must be [B, Hkv, T, D] = [{B}, Hkv, {T}, {D}]; "
-                         f"got {tuple(k.shape)} and {tuple(v.shape)}")
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D \
+            or (same_rows and k.shape[2] != T):
+        rows = "T" if same_rows else "Tk"
+        raise ValueError(f"k, v must be [B, Hkv, {rows}, D] with B={B}, D={D}"
+                         + (f", T={T}" if same_rows else "")
+                         + f"; got {tuple(k.shape)} and {tuple(v.shape)}")
     return B, Hq, k.shape[1], T, D
 
 
@@ -142,4 +154,49 @@ def attn_fwd(q, k, v, causal: bool = True, scale: float | None = None):
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     attn_fwd_into(q, k, v, out, lse, causal, scale)
+    return out, lse
+
+
+def attn_fwd_kv_into(q, k, v, out, lse, causal: bool = True, scale: float | None = None,
+                     stream=None) -> None:
+    """tessera_attn_fwd_kv: q [B,Hq,Tq,D] against the keys and values k, v
+    [B,Hkv,Tk,D] (bfloat16), query row i standing at position i + Tk - Tq;
+    writes `out` [B,Hq,Tq,D] bfloat16 and `lse` [B,Hq,Tq] float32.  Enqueued on
+    `stream` (default: the current torch stream of q's device)."""
+    import torch
+
+    B, Hq, Hkv, Tq, D = _check_inputs(q, k, v, same_rows=False)
+    Tk = k.shape[2]
+    if q.dtype != torch.bfloat16:
+        raise ValueError("attn_fwd_kv takes bfloat16 q, k, v")
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32 or lse.device != q.device \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Tq] on q's device")
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = raw_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr(), B, Hq, Hkv, Tq, Tk, D, int(bool(causal)), scale, handle)
+    if st != OK:
+        msg = status_string(st)
+        if st == ERR_LAUNCH:
+            msg += ": " + lib().tessera_attn_last_error().decode()
+        raise RuntimeError(f"tessera_attn_fwd_kv failed ({st}): {msg}")
+
+
+def attn_fwd_kv(q, k, v, causal: bool = True, scale: float | None = None):
+    """Attention of Tq new query rows against Tk cached key/value rows
+    (bfloat16).  Returns (out [B,Hq,Tq,D], lse [B,Hq,Tq] float32)."""
+    import torch
+
+    B, Hq, Hkv, Tq, D = _check_inputs(q, k, v, same_rows=False)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    attn_fwd_kv_into(q, k, v, out, lse, causal, scale)
     return out, lse

@@ -21,7 +21,7 @@
 
 #include "tessera_attn.h"
 
-#define TESSERA_VERSION 10000
+#define TESSERA_VERSION 10100
 
 namespace {
 
@@ -75,7 +75,9 @@ struct Bf16Args {
     const uint16_t *q, *k, *v;
     uint16_t *o;
     float *lse;
-    int Hq, Hkv, T, G;
+    int Hq, Hkv, G;
+    int Tq, Tk;   // query rows and key rows per head
+    int qoff;     // query row i stands at key position i + qoff (qoff = Tk - Tq)
     int hg;       // heads of one GQA group handled by a workgroup
     int nqb;      // 32-row query blocks per workgroup (kWaves / hg)
     int nslots;   // workgroups sharing one (query tile, KV head): G / hg
@@ -124,8 +126,8 @@ struct LdsRing {
 // fills LDS chunk slots [64i, 64i + 64) -- slot p by lane p%64 -- so each lane
 // fetches the logical chunk that the swizzle places in its slot.  The per-lane
 // byte offsets within a tile are fixed; only the tile's base row moves.  Rows
-// past T (last, ragged tile) are clamped to row T-1: they only ever meet
-// masked scores.
+// past the last key row Tk-1 (last, ragged tile) are clamped to it: they only
+// ever meet masked scores.
 template <int D, bool IS_V, int NW>
 struct TileLoader {
     static constexpr int kRowBytes = D * 2;
@@ -148,8 +150,8 @@ struct TileLoader {
         return kLoadsPerTile % NW == 0 || wi + NW * r < kLoadsPerTile;
     }
     // Load r alone, for the tile whose row 0 is at base.  With CLAMP, rows past
-    // `last` (T - 1 - j0, which may exceed the tile) are clamped to row `last`;
-    // without, the caller guarantees that every row of the tile is below T.
+    // `last` (Tk - 1 - j0, which may exceed the tile) are clamped to row `last`;
+    // without, the caller guarantees that every row of the tile is below Tk.
     template <bool CLAMP>
     __device__ __forceinline__ void load_one(int r, LDS_AS char *dst, const char *base,
                                              int last) const {
@@ -162,15 +164,15 @@ struct TileLoader {
         dma16(base, o, (uint32_t)(uintptr_t)dst + 1024 * (wi + NW * r));
     }
     __device__ __forceinline__ void load(LDS_AS char *dst, const uint16_t *head, int j0,
-                                         int T) const {
+                                         int Tk) const {
         const char *base = (const char *)(head + (int64_t)j0 * D);
         const uint32_t lds = (uint32_t)(uintptr_t)dst;
-        if (j0 + kKeyTile <= T) {
+        if (j0 + kKeyTile <= Tk) {
 #pragma unroll
             for (int r = 0; r < kPerWave; ++r)
                 if (active(r)) dma16(base, off[r], lds + 1024 * (wi + NW * r));
         } else {
-            const int last = T - 1 - j0;   // last valid row of this tile
+            const int last = Tk - 1 - j0;   // last valid row of this tile
 #pragma unroll
             for (int r = 0; r < kPerWave; ++r) {
                 if (!active(r)) continue;
@@ -185,7 +187,7 @@ struct TileLoader {
 // The K/V loads that ride in one MFMA phase: this wave's share of one K tile
 // and one V tile, issued in kSteps single loads spread over the phase.  Step 0
 // first waits for the loads this wave issued in its previous MFMA phase.
-// RAGGED: T is not a multiple of the key tile, so a tile may cross T.
+// RAGGED: Tk is not a multiple of the key tile, so a tile may cross Tk.
 template <int D, bool RAGGED>
 struct PhaseLoads {
     static constexpr int kPer = TileLoader<D, false, kWaves>::kPerWave;
@@ -426,9 +428,9 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, uint32_t vrel,
 // four-deep LDS ring with direct global->LDS loads issued between the MFMAs;
 // the schedule of loads, waits and reads is spelled out at the loop below,
 // which is unrolled by four so every LDS buffer is a distinct array.
-// RAGGED: T % kKeyTile != 0 (the last key tile crosses T).
+// RAGGED: Tk % kKeyTile != 0 (the last key tile crosses Tk).
 // PAIRED: two workgroups per CU (four waves per SIMD, at most 128 VGPRs each;
-// D = 64 with T a multiple of the key tile only: the LDS ring is 64 KB, and
+// D = 64 with Tk a multiple of the key tile only: the LDS ring is 64 KB, and
 // the ragged build would spill in the loop).  The two run independently, so the
 // vector phases of one overlap the matrix-core phases of the other on top of
 // the ping-pong inside each: the vector work of a single wave is bound by its
@@ -437,7 +439,7 @@ template <int D, bool RAGGED, bool PAIRED>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(PAIRED ? 4 : 2)))
 attn_fwd_bf16_kernel(Bf16Args a) {
-    static_assert(!PAIRED || (D == 64 && !RAGGED), "two workgroups per CU: D = 64, T % 64 == 0");
+    static_assert(!PAIRED || (D == 64 && !RAGGED), "two workgroups per CU: D = 64, Tk % 64 == 0");
     __shared__ LdsRing<D> lds;
 
     const int tid = threadIdx.x;
@@ -460,33 +462,35 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     const int q0 = qt * rows_wg;
     const int qw0 = q0 + 32 * (w / a.hg);
     const int query = qw0 + col;
-    const int T = a.T;
+    const int Tq = a.Tq, Tk = a.Tk, qoff = a.qoff;
     const bool causal = a.causal != 0;
 
-    const int64_t q_row0 = ((int64_t)b * a.Hq + head) * T;
-    const uint16_t *khead = a.k + (int64_t)bh * T * D;
-    const uint16_t *vhead = a.v + (int64_t)bh * T * D;
+    const int64_t q_row0 = ((int64_t)b * a.Hq + head) * Tq;
+    const uint16_t *khead = a.k + (int64_t)bh * Tk * D;
+    const uint16_t *vhead = a.v + (int64_t)bh * Tk * D;
 
-    const int q_end = min(q0 + rows_wg, T);
-    const int kv_end = causal ? q_end : T;
+    // Causal: query row i sees keys 0 .. i + qoff, so the workgroup's last row
+    // sees up to key q_end - 1 + qoff (at most Tk - 1).
+    const int q_end = min(q0 + rows_wg, Tq);
+    const int kv_end = causal ? q_end + qoff : Tk;
     const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
 
     // Prologue loads, shared by all waves: K(0), K(1), K(2), V(0), V(1).
     {
         const TileLoader<D, false, kWaves> kl(w, lane);
         const TileLoader<D, true, kWaves> vl(w, lane);
-        kl.load((LDS_AS char *)lds.k[0], khead, 0, T);
-        if (ntiles > 1) kl.load((LDS_AS char *)lds.k[1], khead, kKeyTile, T);
-        if (ntiles > 2) kl.load((LDS_AS char *)lds.k[2], khead, 2 * kKeyTile, T);
-        vl.load((LDS_AS char *)lds.v[0], vhead, 0, T);
-        if (ntiles > 1) vl.load((LDS_AS char *)lds.v[1], vhead, kKeyTile, T);
+        kl.load((LDS_AS char *)lds.k[0], khead, 0, Tk);
+        if (ntiles > 1) kl.load((LDS_AS char *)lds.k[1], khead, kKeyTile, Tk);
+        if (ntiles > 2) kl.load((LDS_AS char *)lds.k[2], khead, 2 * kKeyTile, Tk);
+        vl.load((LDS_AS char *)lds.v[0], vhead, 0, Tk);
+        if (ntiles > 1) vl.load((LDS_AS char *)lds.v[1], vhead, kKeyTile, Tk);
     }
 
     // Q fragment (B operand of S^T = K Q^T): lane holds 8 dims of its query
-    // row per 16-dim step.  Rows past T are clamped; their results are dropped.
+    // row per 16-dim step.  Rows past Tq are clamped; their results are dropped.
     bf16x8 qf[D / 16];
     {
-        const uint16_t *src = a.q + (q_row0 + min(query, T - 1)) * D + 8 * hi;
+        const uint16_t *src = a.q + (q_row0 + min(query, Tq - 1)) * D + 8 * hi;
         const uint32_t flip = a.qmode == 1 ? 0x80008000u : 0u;
         const uint32_t keep = a.qmode == 2 ? 0u : 0xffffffffu;
 #pragma unroll
@@ -514,11 +518,11 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     // `first`: tile 0 (m is still -inf there; afterwards m is finite).
     auto softmax_phase = [&](int t, bool first) __attribute__((always_inline)) {
         const int j0 = t * kKeyTile;
-        // Mask keys hidden from a query (diagonal tile) or past T (ragged tile).
-        if ((RAGGED && j0 + kKeyTile > T) || (causal && j0 + kKeyTile - 1 > qw0)) {
+        // Mask keys hidden from a query (diagonal tile) or past Tk (ragged tile).
+        if ((RAGGED && j0 + kKeyTile > Tk) || (causal && j0 + kKeyTile - 1 > qw0 + qoff)) {
             // Row i of this lane is key j0 + 4*hi + 8*(i/4) + i%4 (+32 in s1);
             // it is visible iff that key <= last, the last key this query sees.
-            const int last = (causal ? min(query, T - 1) : T - 1) - j0 - 4 * hi;
+            const int last = (causal ? min(query, Tq - 1) + qoff : Tk - 1) - j0 - 4 * hi;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = 8 * (i >> 2) + (i & 3);
@@ -600,8 +604,8 @@ attn_fwd_bf16_kernel(Bf16Args a) {
                              vw,
                              (const char *)(khead + (int64_t)tk * kKeyTile * D),
                              (const char *)(vhead + (int64_t)tv * kKeyTile * D),
-                             T - 1 - tk * kKeyTile,
-                             T - 1 - tv * kKeyTile};
+                             Tk - 1 - tk * kKeyTile,
+                             Tk - 1 - tv * kKeyTile};
     };
     u32x4 ring[kPrefetch];   // operands of the next MFMA phase's first ops
     // Buffers are named by index: K tile b at lds.k[b], V tile b at byte offset
@@ -663,7 +667,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     const int hi_e = lane_e >> 5;
     const int query_e = qw0 + (lane_e & 31);
     const float l_tot = ((lane_e >> 4) & 1) ? lsum[1] : lsum[0];
-    if (query_e < T) {
+    if (query_e < Tq) {
         const float inv = 1.f / l_tot;
         uint16_t *dst = a.o + (q_row0 + query_e) * D;
 #pragma unroll
@@ -768,17 +772,18 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 int validate(const void *q, const void *k, const void *v, const void *out, const void *lse,
-             int B, int Hq, int Hkv, int T, int D, int causal, float scale, size_t elem) {
+             int B, int Hq, int Hkv, int Tq, int Tk, int D, int causal, float scale, size_t elem) {
     if (!q || !k || !v || !out || !lse) return TESSERA_ERR_NULL;
-    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Hq % Hkv != 0) return TESSERA_ERR_SHAPE;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || Tk < 1 || Hq % Hkv != 0) return TESSERA_ERR_SHAPE;
     if (D != 32 && D != 64 && D != 128) return TESSERA_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1) return TESSERA_ERR_CAUSAL;
+    if (causal == 1 && Tq > Tk) return TESSERA_ERR_SHAPE;
     if (!isfinite(scale)) return TESSERA_ERR_SCALE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return TESSERA_ERR_ALIGN;
     if ((uintptr_t)lse & 3u) return TESSERA_ERR_ALIGN;
-    const size_t qbytes = (size_t)B * Hq * T * D * elem;
-    const size_t kvbytes = (size_t)B * Hkv * T * D * elem;
-    const size_t lbytes = (size_t)B * Hq * T * sizeof(float);
+    const size_t qbytes = (size_t)B * Hq * Tq * D * elem;
+    const size_t kvbytes = (size_t)B * Hkv * Tk * D * elem;
+    const size_t lbytes = (size_t)B * Hq * Tq * sizeof(float);
     if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kvbytes) ||
         overlaps(out, qbytes, v, kvbytes) || overlaps(lse, lbytes, q, qbytes) ||
         overlaps(lse, lbytes, k, kvbytes) || overlaps(lse, lbytes, v, kvbytes) ||
@@ -794,14 +799,9 @@ int launch_status(void) {
     return TESSERA_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" int tessera_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
-                                int B, int Hq, int Hkv, int T, int D, int causal, float scale,
-                                void *stream) {
-    const int st = validate(q, k, v, out, lse, B, Hq, Hkv, T, D, causal, scale, 2);
-    if (st != TESSERA_OK) return st;
-
+// The bf16 launch shared by both entry points (arguments already validated).
+int launch_bf16(const void *q, const void *k, const void *v, void *out, float *lse, int B,
+                int Hq, int Hkv, int Tq, int Tk, int D, int causal, float scale, void *stream) {
     Bf16Args a;
     a.q = (const uint16_t *)q;
     a.k = (const uint16_t *)k;
@@ -810,12 +810,14 @@ extern "C" int tessera_attn_fwd(const void *q, const void *k, const void *v, voi
     a.lse = lse;
     a.Hq = Hq;
     a.Hkv = Hkv;
-    a.T = T;
+    a.Tq = Tq;
+    a.Tk = Tk;
+    a.qoff = Tk - Tq;
     a.G = Hq / Hkv;
     a.hg = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
     a.nqb = kWaves / a.hg;
     a.nslots = a.G / a.hg;
-    a.nqt = (T + 32 * a.nqb - 1) / (32 * a.nqb);
+    a.nqt = (Tq + 32 * a.nqb - 1) / (32 * a.nqb);
     const int64_t grid = (int64_t)a.nqt * B * Hkv * a.nslots;
     if (grid > 0x7fffffff) return TESSERA_ERR_TOO_LARGE;
     a.nbh = B * Hkv;
@@ -825,7 +827,7 @@ extern "C" int tessera_attn_fwd(const void *q, const void *k, const void *v, voi
 
     hipStream_t s = (hipStream_t)stream;
     const dim3 g((unsigned)grid), blk(kThreads);
-    const bool ragged = T % kKeyTile != 0;
+    const bool ragged = Tk % kKeyTile != 0;
     // Two workgroups per CU pay off once the grid covers the 512 slots of 256
     // CUs several times over; on a grid that fills them about once, the pairs
     // that land together are too uneven in length (causal tiles differ).
@@ -845,10 +847,28 @@ extern "C" int tessera_attn_fwd(const void *q, const void *k, const void *v, voi
     return launch_status();
 }
 
+}  // namespace
+
+extern "C" int tessera_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+                                int B, int Hq, int Hkv, int T, int D, int causal, float scale,
+                                void *stream) {
+    const int st = validate(q, k, v, out, lse, B, Hq, Hkv, T, T, D, causal, scale, 2);
+    if (st != TESSERA_OK) return st;
+    return launch_bf16(q, k, v, out, lse, B, Hq, Hkv, T, T, D, causal, scale, stream);
+}
+
+extern "C" int tessera_attn_fwd_kv(const void *q, const void *k, const void *v, void *out,
+                                   float *lse, int B, int Hq, int Hkv, int Tq, int Tk, int D,
+                                   int causal, float scale, void *stream) {
+    const int st = validate(q, k, v, out, lse, B, Hq, Hkv, Tq, Tk, D, causal, scale, 2);
+    if (st != TESSERA_OK) return st;
+    return launch_bf16(q, k, v, out, lse, B, Hq, Hkv, Tq, Tk, D, causal, scale, stream);
+}
+
 extern "C" int tessera_attn_fwd_f32(const float *q, const float *k, const float *v, float *out,
                                     float *lse, int B, int Hq, int Hkv, int T, int D, int causal,
                                     float scale, void *stream) {
-    const int st = validate(q, k, v, out, lse, B, Hq, Hkv, T, D, causal, scale, 4);
+    const int st = validate(q, k, v, out, lse, B, Hq, Hkv, T, T, D, causal, scale, 4);
     if (st != TESSERA_OK) return st;
     const int ntiles = (T + kF32Rows - 1) / kF32Rows;
     const int64_t grid = (int64_t)ntiles * B * Hq;
@@ -870,7 +890,9 @@ extern "C" const char *tessera_attn_status_string(int status) {
     switch (status) {
     case TESSERA_OK: return "ok";
     case TESSERA_ERR_NULL: return "null pointer argument";
-    case TESSERA_ERR_SHAPE: return "bad shape: B, Hq, Hkv, T must be >= 1 and Hq % Hkv == 0";
+    case TESSERA_ERR_SHAPE:
+        return "bad shape: B, Hq, Hkv and the row counts must be >= 1, Hq % Hkv == 0, and a "
+               "causal call needs no more query rows than key rows";
     case TESSERA_ERR_UNSUPPORTED: return "unsupported head dim: D must be 32, 64 or 128";
     case TESSERA_ERR_CAUSAL: return "causal must be 0 or 1";
     case TESSERA_ERR_SCALE: return "scale must be finite";

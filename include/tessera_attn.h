@@ -46,7 +46,8 @@ extern "C" {
 enum tessera_attn_status {
     TESSERA_OK = 0,
     TESSERA_ERR_NULL = 1,        /* a pointer argument is NULL */
-    TESSERA_ERR_SHAPE = 2,       /* B, Hq, Hkv or T < 1, or Hq % Hkv != 0 */
+    TESSERA_ERR_SHAPE = 2,       /* B, Hq, Hkv or a row count < 1, Hq % Hkv != 0, or a
+                                    causal tessera_attn_fwd_kv call with Tq > Tk */
     TESSERA_ERR_UNSUPPORTED = 3, /* D is not 32, 64 or 128 */
     TESSERA_ERR_CAUSAL = 4,      /* causal is neither 0 nor 1 */
     TESSERA_ERR_SCALE = 5,       /* scale is NaN or infinite */
@@ -66,6 +67,28 @@ enum tessera_attn_status {
 int tessera_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
                      int B, int Hq, int Hkv, int T, int D, int causal, float scale,
                      void *stream);
+
+/*
+ * bf16 attention forward of Tq query rows against Tk key rows (Tq <= Tk when
+ * causal): the continuation of a sequence whose first Tk - Tq positions are
+ * already in the K/V cache, as in chunked prefill or decoding a few tokens.
+ * The page "Tessera: a from-scratch distillation and serving stack in one
+ * repository" (section "Serving: block-paged KV, batch recomposition,
+ * speculation") states the property this serves: decoding incrementally with
+ * the KV cache gives what a full forward pass gives.  Query row i stands at
+ * sequence position i + Tk - Tq, so with causal = 1 it sees keys
+ * j <= i + Tk - Tq (the causal mask aligned to the last key); with causal = 0
+ * it sees all Tk keys, and any Tq, Tk >= 1 is accepted.  Row i of the result
+ * equals row i + Tk - Tq of tessera_attn_fwd run on the full sequence.
+ *     q   [B, Hq,  Tq, D]     k, v [B, Hkv, Tk, D]
+ *     out [B, Hq,  Tq, D]     lse  [B, Hq,  Tq]
+ * Everything else (dtypes, scale, ownership, streams, errors) is as for
+ * tessera_attn_fwd; tessera_attn_fwd(..., T, ...) is this call with
+ * Tq = Tk = T.
+ */
+int tessera_attn_fwd_kv(const void *q, const void *k, const void *v, void *out, float *lse,
+                        int B, int Hq, int Hkv, int Tq, int Tk, int D, int causal, float scale,
+                        void *stream);
 
 /*
  * fp32 attention forward: the same operation and arguments with float32

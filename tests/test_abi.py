@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_symbol():
     lib = binding.lib()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert binding.version() == 10000
+    assert binding.version() == 10100
 
 
 def test_status_strings():
