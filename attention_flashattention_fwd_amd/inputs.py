@@ -74,6 +74,51 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class KVWorkload:
+    """Tq new query rows against Tk cached key rows (tessera_attn_fwd_kv).  The
+    tensors are the last Tq query rows of the full T = Tk workload drawn with
+    the same recipe, so every output row is also a row of that full forward."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Tq: int
+    Tk: int
+    D: int
+    dtype: str = "bf16"
+    causal: bool = True
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.D)
+
+    @property
+    def pairs(self) -> float:
+        """Visible (query, key) pairs per head: row i sees i + Tk - Tq + 1 keys."""
+        if not self.causal:
+            return float(self.Tq) * self.Tk
+        off = self.Tk - self.Tq
+        return float(self.Tq) * off + self.Tq * (self.Tq + 1) / 2
+
+    @property
+    def flops(self) -> float:
+        """4*D per visible pair, counted exactly."""
+        return 4.0 * self.B * self.Hq * self.D * self.pairs
+
+    def describe(self) -> str:
+        return (f"B={self.B} Hq={self.Hq} Hkv={self.Hkv} Tq={self.Tq} Tk={self.Tk} D={self.D} "
+                f"{self.dtype} causal={int(self.causal)}")
+
+
+# Continuation workloads: the last 2048-row chunk of the 16k sequence
+# (chunked prefill against a 14k-token cache).
+KV_WORKLOADS = {
+    "chunk2048_t16384_d128": KVWorkload("chunk2048_t16384_d128", 1, 32, 8, 2048, 16384, 128),
+}
+
+
 def default_scale(D: int) -> float:
     """The fp32 value of 1/sqrt(D), returned as a Python float."""
     return float(np.float32(1.0 / math.sqrt(D)))
@@ -105,6 +150,16 @@ def make_qkv(B, Hq, Hkv, T, D, dtype="bf16", seed=0, outliers=""):
 
 def make_workload(w: Workload):
     return make_qkv(w.B, w.Hq, w.Hkv, w.T, w.D, w.dtype, w.seed, w.outliers)
+
+
+def make_kv_workload(w: KVWorkload, full_q: bool = False):
+    """(q, k, v) of a continuation workload: q holds the last Tq rows of the
+    full query tensor (all Tk rows when full_q, for checks against a full
+    forward)."""
+    q, k, v = make_qkv(w.B, w.Hq, w.Hkv, w.Tk, w.D, w.dtype, w.seed)
+    if not full_q:
+        q = q[:, :, w.Tk - w.Tq:].contiguous()
+    return q, k, v
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

@@ -35,7 +35,7 @@ sys.path.insert(0, str(ROOT))
 PEAK_BF16_TFLOPS = 2516.6     # dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "t16384_d128"
-SECONDARY = ["t4096_outliers", "t2048", "t2048_full"]
+SECONDARY = ["t4096_outliers", "t2048", "t2048_full", "chunk2048_t16384_d128"]
 KERNEL_SOURCE = ROOT / "attention_flashattention_fwd_amd" / "csrc" / "tessera_attn.hip"
 TRAFFIC_SUMMARY = ROOT / "profiles" / "hbm_traffic_attn_fwd_bf16_t16384_d128.md"
 
@@ -226,14 +226,23 @@ def main(argv=None):
         return 0
 
     def measure(name, steps, warmup, with_cpu, warm_seconds=0.0):
-        w = inputs.WORKLOADS[name]
-        q, k, v = inputs.make_workload(w)
-        qd, kd, vd = (t.to(dev) for t in (q, k, v))
-        out = torch.empty_like(qd)
-        lse = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev)
+        if name in inputs.KV_WORKLOADS:   # Tq new rows against Tk cached rows
+            w = inputs.KV_WORKLOADS[name]
+            q, k, v = inputs.make_kv_workload(w)
+            qd, kd, vd = (t.to(dev) for t in (q, k, v))
+            out = torch.empty_like(qd)
+            lse = torch.empty((w.B, w.Hq, w.Tq), dtype=torch.float32, device=dev)
+            fn = lambda: binding.attn_fwd_kv_into(qd, kd, vd, out, lse,  # noqa: E731
+                                                  w.causal, w.scale, stream=stream)
+        else:
+            w = inputs.WORKLOADS[name]
+            q, k, v = inputs.make_workload(w)
+            qd, kd, vd = (t.to(dev) for t in (q, k, v))
+            out = torch.empty_like(qd)
+            lse = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev)
+            fn = lambda: binding.attn_fwd_into(qd, kd, vd, out, lse,  # noqa: E731
+                                               w.causal, w.scale, stream=stream)
         torch.cuda.synchronize()
-        fn = lambda: binding.attn_fwd_into(qd, kd, vd, out, lse, w.causal, w.scale,  # noqa: E731
-                                           stream=stream)
         gpu_ms, wall_ms, med_ms, min_ms = time_steps(torch, fn, steps, warmup, stream,
                                                      warm_seconds)
         res = {"w": w, "gpu_ms": gpu_ms, "wall_ms": wall_ms, "med_ms": med_ms, "min_ms": min_ms}
@@ -241,7 +250,12 @@ def main(argv=None):
             res["cpu"], res["parity"] = cpu_baseline(w, q, k, v, out, lse, args.cpu_seconds)
         return res
 
-    head = measure(args.workload, args.steps, args.warmup, not args.no_cpu)
+    if args.workload not in inputs.WORKLOADS and args.workload not in inputs.KV_WORKLOADS:
+        print(f"unknown workload {args.workload!r}", file=sys.stderr)
+        return 2
+    # the CPU leg samples rows of full-sequence workloads only
+    head = measure(args.workload, args.steps, args.warmup,
+                   not args.no_cpu and args.workload in inputs.WORKLOADS)
     w = head["w"]
     tflops = w.flops / (head["wall_ms"] * 1e-3) / 1e12
     achieved = w.flops / (head["gpu_ms"] * 1e-3) / 1e12
@@ -276,9 +290,11 @@ def main(argv=None):
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, bf16)",
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "D": w.D,
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   **({"T": w.T} if hasattr(w, "T") else {"Tq": w.Tq, "Tk": w.Tk}), "D": w.D,
                    "causal": w.causal, "scale": w.scale, "flops_per_step": w.flops,
-                   "pair_exact_flops_per_step": w.pair_flops, "parallelism": "single GPU"},
+                   "pair_exact_flops_per_step": getattr(w, "pair_flops", w.flops),
+                   "parallelism": "single GPU"},
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

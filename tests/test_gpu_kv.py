@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from attention_flashattention_fwd_amd import binding, inputs
-from tests.test_gpu_parity import check_close, say
+from tests.test_gpu_parity import check_close, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -98,3 +98,27 @@ def test_kv_argument_checks():
     assert out.shape == q.shape and lse.shape == (1, 4, 10)
     with pytest.raises(ValueError):
         binding.attn_fwd_kv(q.float(), k.float(), v.float())
+
+
+@pytest.mark.parametrize("name", sorted(inputs.KV_WORKLOADS))
+def test_kv_full_size_workload(name):
+    """The benchmarked continuation workload at its real size: sampled rows
+    against the oracle's rows of the full forward they belong to."""
+    w = inputs.KV_WORKLOADS[name]
+    say(f"workload {name}: {w.describe()}")
+    q_full, k, v = inputs.make_kv_workload(w, full_q=True)
+    q = q_full[:, :, w.Tk - w.Tq:].contiguous()
+    dev = torch.device("cuda:0")
+    out, lse = binding.attn_fwd_kv(q.to(dev), k.to(dev), v.to(dev), causal=w.causal,
+                                   scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rows = sample_rows(w.B, w.Hq, w.Tq, 400, seed=len(name))   # flat (b*Hq + h)*Tq + i
+    bh, i = rows // w.Tq, rows % w.Tq
+    full_rows = bh * w.Tk + i + (w.Tk - w.Tq)
+    say(f"oracle on {len(rows)} sampled rows")
+    O_ref, l_ref = oracle.attn_rows(inputs.bits(q_full), inputs.bits(k), inputs.bits(v),
+                                    w.causal, w.scale, full_rows)
+    o = out.reshape(-1, w.D)[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+    l = lse.reshape(-1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    check_close(o.astype(np.float64), l.astype(np.float64), O_ref, l_ref, w.dtype, name)

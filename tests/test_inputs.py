@@ -49,3 +49,20 @@ def test_workload_table():
     assert abs(w.flops - 2.199e12) / 2.199e12 < 1e-3
     assert inputs.default_scale(128) == float(np.float32(1 / np.sqrt(128)))
     assert inputs.WORKLOADS["fp32_t64"].dtype == "fp32"
+
+
+def test_kv_workload_counts_and_rows():
+    """A continuation workload counts i + Tk - Tq + 1 visible keys for row i,
+    reduces to the full count when Tq = Tk, and takes the last Tq query rows
+    of the full draw."""
+    w = inputs.KVWorkload("x", 1, 2, 1, 3, 5, 8)
+    assert w.pairs == (2 + 1) + (2 + 2) + (2 + 3)   # Tk - Tq = 2
+    full = inputs.KVWorkload("y", 2, 4, 2, 7, 7, 16)
+    same = inputs.Workload("y", 2, 4, 2, 7, 16, "bf16", True)
+    assert full.flops == same.pair_flops
+    assert inputs.KVWorkload("z", 1, 2, 1, 3, 5, 8, causal=False).pairs == 15
+    small = inputs.KVWorkload("s", 1, 2, 1, 4, 9, 8)
+    q, k, v = inputs.make_kv_workload(small)
+    qf, kf, vf = inputs.make_qkv(1, 2, 1, 9, 8, "bf16", 0)
+    assert q.shape == (1, 2, 4, 8) and k.shape == (1, 1, 9, 8)
+    assert torch.equal(q, qf[:, :, 5:]) and torch.equal(k, kf) and torch.equal(v, vf)
