@@ -11,5 +11,6 @@ from .oracle import (  # noqa: F401
     attn_rows,
     build,
     load,
+    rmsnorm,
     threads,
 )

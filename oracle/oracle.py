@@ -18,6 +18,7 @@ import numpy as np
 
 HERE = Path(__file__).resolve().parent
 SOURCE = HERE / "attn_oracle.c"
+RMS_SOURCE = HERE / "rmsnorm_oracle.c"
 LIBRARY = HERE / "liboracle_attn.so"
 
 DTYPE_F32 = 0
@@ -27,10 +28,10 @@ _c_double_p = ctypes.POINTER(ctypes.c_double)
 _c_int64_p = ctypes.POINTER(ctypes.c_int64)
 
 
-def build(source: Path = SOURCE, output: Path = LIBRARY) -> Path:
+def build(source: Path = SOURCE, output: Path = LIBRARY, rms_source: Path = RMS_SOURCE) -> Path:
     """Compile the oracle with gcc (plain -O2, OpenMP) into a shared library."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-           str(source), "-o", str(output) + ".tmp", "-lm"]
+           str(source), str(rms_source), "-o", str(output) + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(str(output) + ".tmp", output)
     return output
@@ -55,6 +56,9 @@ class OracleLib:
         lib.tessera_oracle_attn_rows.restype = ctypes.c_int
         lib.tessera_oracle_attn_probs.argtypes = common + [_c_double_p, _c_double_p, _c_double_p]
         lib.tessera_oracle_attn_probs.restype = ctypes.c_int
+        lib.tessera_oracle_rmsnorm.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.c_int, ctypes.c_double, _c_double_p]
+        lib.tessera_oracle_rmsnorm.restype = ctypes.c_int
         lib.tessera_oracle_threads.argtypes = [ctypes.c_int]
         lib.tessera_oracle_threads.restype = ctypes.c_int
         self.lib = lib
@@ -142,6 +146,20 @@ class OracleLib:
         self._check(rc, "tessera_oracle_attn_probs")
         return O, lse, P
 
+    def rmsnorm(self, x, w, eps: float):
+        """x [rows, n] and w [n] as uint16 bf16 patterns; returns y [rows, n] fp64."""
+        x = np.ascontiguousarray(x)
+        w = np.ascontiguousarray(w)
+        if x.dtype != np.uint16 or w.dtype != np.uint16:
+            raise ValueError("rmsnorm oracle takes uint16 bf16 patterns")
+        if x.ndim != 2 or w.ndim != 1 or w.shape[0] != x.shape[1]:
+            raise ValueError("x must be [rows, n] and w [n]")
+        y = np.empty(x.shape, np.float64)
+        rc = self.lib.tessera_oracle_rmsnorm(self._ptr(x), self._ptr(w), x.shape[0], x.shape[1],
+                                             float(eps), y.ctypes.data_as(_c_double_p))
+        self._check(rc, "tessera_oracle_rmsnorm")
+        return y
+
     def threads(self, nthreads: int = 0) -> int:
         return int(self.lib.tessera_oracle_threads(int(nthreads)))
 
@@ -153,7 +171,8 @@ def load() -> OracleLib:
     """The oracle built from attn_oracle.c (compiled on first use if absent)."""
     global _DEFAULT
     if _DEFAULT is None:
-        if not LIBRARY.exists() or LIBRARY.stat().st_mtime < SOURCE.stat().st_mtime:
+        newest = max(SOURCE.stat().st_mtime, RMS_SOURCE.stat().st_mtime)
+        if not LIBRARY.exists() or LIBRARY.stat().st_mtime < newest:
             build()
         _DEFAULT = OracleLib(LIBRARY)
     return _DEFAULT
@@ -173,6 +192,10 @@ def attn_rows(q, k, v, causal, scale, rows, nthreads=0):
 
 def attn_probs(q, k, v, causal, scale):
     return load().attn_probs(q, k, v, causal, scale)
+
+
+def rmsnorm(x, w, eps):
+    return load().rmsnorm(x, w, eps)
 
 
 def threads(nthreads=0):

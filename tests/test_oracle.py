@@ -9,9 +9,10 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.oracle import OracleLib, SOURCE
+from oracle.oracle import RMS_SOURCE, SOURCE, OracleLib
 from tests import oracle_pins
 from tests.oracle_pins import ALL_PINS, rand_inputs
+from tests.rmsnorm_pins import ALL_RMS_PINS
 
 
 @pytest.fixture(scope="module")
@@ -19,7 +20,7 @@ def lib():
     return oracle.load()
 
 
-@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", ALL_PINS + ALL_RMS_PINS, ids=lambda f: f.__name__)
 def test_pin(lib, pin):
     pin(lib)
 
@@ -53,17 +54,54 @@ MUTANTS = {
 }
 
 
+# The same for the RMSNorm oracle.
+RMS_MUTANTS = {
+    "sum_not_mean": ("const double ms = ss / n;", "const double ms = ss;"),
+    "eps_outside_sqrt": ("1.0 / sqrt(ms + eps)", "1.0 / (sqrt(ms) + eps)"),
+    "no_sqrt": ("1.0 / sqrt(ms + eps)", "1.0 / (ms + eps)"),
+    "gain_dropped": ("* inv * widen_bf16(w[c]);", "* inv;"),
+    "gain_shifted": ("* inv * widen_bf16(w[c]);", "* inv * widen_bf16(w[(c + 1) % n]);"),
+    "abs_not_square": ("ss += v * v;", "ss += fabs(v);"),
+    "last_column_skipped": ("for (int c = 0; c < n; ++c) {\n            const double v",
+                            "for (int c = 0; c < n - 1; ++c) {\n            const double v"),
+}
+
+
+def build_mutant(tmp_path: Path, attn_src: str, rms_src: str) -> OracleLib:
+    a, r = tmp_path / "mutant_attn.c", tmp_path / "mutant_rms.c"
+    a.write_text(attn_src)
+    r.write_text(rms_src)
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", str(a), str(r),
+                    "-o", str(so), "-lm"], check=True)
+    return OracleLib(so)
+
+
+def caught_by(mutant, pins):
+    caught = []
+    for pin in pins:
+        try:
+            pin(mutant)
+        except (AssertionError, RuntimeError, ValueError):
+            caught.append(pin.__name__)
+    return caught
+
+
+@pytest.mark.parametrize("name", sorted(RMS_MUTANTS))
+def test_planted_rmsnorm_mistake_is_caught(tmp_path: Path, name):
+    old, new = RMS_MUTANTS[name]
+    src = RMS_SOURCE.read_text()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutant = build_mutant(tmp_path, SOURCE.read_text(), src.replace(old, new, 1))
+    assert caught_by(mutant, ALL_RMS_PINS), f"no pin rejects the planted mistake {name}"
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(tmp_path: Path, name):
     old, new = MUTANTS[name]
     src = SOURCE.read_text()
     assert src.count(old) >= 1, f"mutation anchor for {name} not found"
-    mutated = tmp_path / "mutant.c"
-    mutated.write_text(src.replace(old, new, 1))
-    so = tmp_path / "libmutant.so"
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", str(mutated),
-                    "-o", str(so), "-lm"], check=True)
-    mutant = OracleLib(so)
+    mutant = build_mutant(tmp_path, src.replace(old, new, 1), RMS_SOURCE.read_text())
     caught = []
     for pin in ALL_PINS:
         try:
