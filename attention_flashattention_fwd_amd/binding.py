@@ -27,9 +27,11 @@ ERR_ALIGN = 6
 ERR_ALIAS = 7
 ERR_TOO_LARGE = 8
 ERR_LAUNCH = 9
+ERR_EPS = 10
 
 EXPORTS = ("tessera_attn_fwd", "tessera_attn_fwd_kv", "tessera_attn_fwd_f32",
-           "tessera_attn_status_string", "tessera_attn_last_error", "tessera_attn_version")
+           "tessera_attn_status_string", "tessera_attn_last_error", "tessera_attn_version",
+           "tessera_rmsnorm_fwd")
 
 _lib = None
 
@@ -55,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.tessera_attn_fwd_f32.restype = i
         L.tessera_attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
         L.tessera_attn_fwd_kv.restype = i
+        L.tessera_rmsnorm_fwd.argtypes = [vp, vp, vp, ctypes.c_longlong, i, f, vp]
+        L.tessera_rmsnorm_fwd.restype = i
         L.tessera_attn_status_string.argtypes = [i]
         L.tessera_attn_status_string.restype = ctypes.c_char_p
         L.tessera_attn_last_error.argtypes = []
@@ -200,3 +204,47 @@ def attn_fwd_kv(q, k, v, causal: bool = True, scale: float | None = None):
     lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
     attn_fwd_kv_into(q, k, v, out, lse, causal, scale)
     return out, lse
+
+
+RMSNORM_EPS = 1e-6   # the default gain-normalisation epsilon (the pages give none)
+
+
+def raw_rmsnorm(x, w, y, rows, n, eps, stream) -> int:
+    """Call tessera_rmsnorm_fwd with integer device addresses; returns the status."""
+    return int(lib().tessera_rmsnorm_fwd(x, w, y, int(rows), int(n), float(np.float32(eps)),
+                                         stream))
+
+
+def rmsnorm_fwd_into(x, w, y, eps: float = RMSNORM_EPS, stream=None) -> None:
+    """Fused RMSNorm: y = x / sqrt(mean(x^2, last dim) + eps) * w, bfloat16.
+    x and y are contiguous [..., n] (y may be x), w is [n]."""
+    import torch
+
+    for name, t in (("x", x), ("w", w), ("y", y)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a torch.Tensor on a GPU device")
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    n = x.shape[-1] if x.dim() else 0
+    if w.shape != (n,) or y.shape != x.shape or not (x.device == w.device == y.device):
+        raise ValueError(f"w must be [{n}] and y shaped like x, all on one device")
+    rows = x.numel() // n if n else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(x.device):
+        st = raw_rmsnorm(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, n, eps, handle)
+    if st != OK:
+        msg = status_string(st)
+        if st == ERR_LAUNCH:
+            msg += ": " + lib().tessera_attn_last_error().decode()
+        raise RuntimeError(f"tessera_rmsnorm_fwd failed ({st}): {msg}")
+
+
+def rmsnorm_fwd(x, w, eps: float = RMSNORM_EPS):
+    """Fused RMSNorm of the last dimension of x (bfloat16); returns y like x."""
+    import torch
+
+    y = torch.empty_like(x)
+    rmsnorm_fwd_into(x, w, y, eps)
+    return y

@@ -1,4 +1,5 @@
-"""Build the gfx950 HIP library in-tree: libtessera_attn.so beside this file.
+"""Build the gfx950 HIP library in-tree: libtessera_attn.so beside this file
+(the attention forward and the fused RMSNorm).
 
     python -m attention_flashattention_fwd_amd.build
 """
@@ -12,7 +13,7 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SOURCE = PKG / "csrc" / "tessera_attn.hip"
+SOURCES = [PKG / "csrc" / "tessera_attn.hip", PKG / "csrc" / "tessera_rmsnorm.hip"]
 INCLUDE = ROOT / "include"
 LIBRARY = PKG / "libtessera_attn.so"
 ARCH = "gfx950"
@@ -37,7 +38,8 @@ def hipcc() -> str:
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> Path:
     tmp = LIBRARY.with_suffix(".so.tmp")
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), f"-I{INCLUDE}", str(SOURCE), "-o", str(tmp)]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), f"-I{INCLUDE}", *map(str, SOURCES), "-o",
+           str(tmp)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

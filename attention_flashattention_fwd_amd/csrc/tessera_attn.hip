@@ -900,10 +900,14 @@ extern "C" const char *tessera_attn_status_string(int status) {
     case TESSERA_ERR_ALIAS: return "out or lse overlaps an input or each other";
     case TESSERA_ERR_TOO_LARGE: return "problem too large for one launch grid";
     case TESSERA_ERR_LAUNCH: return "HIP kernel launch failed";
+    case TESSERA_ERR_EPS: return "eps must be finite and non-negative";
     default: return "unknown status";
     }
 }
 
 extern "C" const char *tessera_attn_last_error(void) { return g_last_error; }
+
+// The launch check of this file, for the library's other sources (not exported).
+__attribute__((visibility("hidden"))) int tessera_launch_status(void) { return launch_status(); }
 
 extern "C" int tessera_attn_version(void) { return TESSERA_VERSION; }

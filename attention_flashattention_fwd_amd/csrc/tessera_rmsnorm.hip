@@ -1,0 +1,171 @@
+// tessera_rmsnorm.hip -- gfx950 (MI355X) fused RMSNorm forward and its C ABI
+// (page "Tessera: a from-scratch distillation and serving stack in one
+// repository", section "The kernel set and its torch fallback": the fused
+// RMSNorm of the kernel set).
+//
+//     y[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * w
+//
+// The pass is bound by HBM: every element of x is read once and every
+// element of y written once, 4 bytes per element in bf16, against 3 flops.
+// One wave owns one row at a time: each lane loads 16-byte pieces of the row
+// (consecutive lanes, consecutive pieces, so a wave load covers 1 KB of
+// contiguous memory), squares and sums them in fp32, the wave adds its 64
+// partial sums, and the same registers are scaled and stored.  A wave keeps
+// its pieces of w in registers across all the rows it handles, so w is read
+// once per wave.  Rows of more than 8192 values take a second kernel that
+// reads the row twice (the second time mostly from L2) instead of holding it.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "tessera_rmsnorm.h"
+
+int tessera_launch_status(void);   // tessera_attn.hip
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRowWaves = 4;                 // waves (rows in flight) per workgroup
+constexpr int kThreads = 64 * kRowWaves;
+constexpr int kMaxN = 65536;
+constexpr int kRegMaxVec = 1024;             // 16-byte pieces held in registers: n <= 8192
+constexpr int kMaxGrid = 4096;               // workgroups; waves stride over the rows
+
+// The two bf16 values of a 32-bit word, as fp32 (exact).
+__device__ __forceinline__ float lo_of(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_of(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two fp32 values rounded to bf16 (nearest even) and packed, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const bf16x2 p = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ float squares(const u32x4 &v) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float a = lo_of(v[e]), b = hi_of(v[e]);
+        s = fmaf(a, a, s);
+        s = fmaf(b, b, s);
+    }
+    return s;
+}
+
+__device__ __forceinline__ u32x4 scaled(const u32x4 &v, const u32x4 &g, float rstd) {
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o[e] = pack_bf16(lo_of(v[e]) * rstd * lo_of(g[e]), hi_of(v[e]) * rstd * hi_of(g[e]));
+    return o;
+}
+
+__device__ __forceinline__ float wave_sum(float s) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    return s;
+}
+
+// Rows of nvec <= 64 * VPL pieces, held in registers.
+template <int VPL>
+__global__ void __launch_bounds__(kThreads)
+rmsnorm_reg_kernel(const u32x4 *x, const u32x4 *__restrict__ w,
+                   u32x4 *y, int64_t rows, int nvec, float inv_n, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    u32x4 g[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int c = lane + 64 * i;
+        g[i] = c < nvec ? w[c] : u32x4{};
+    }
+    const int64_t step = (int64_t)gridDim.x * kRowWaves;
+    for (int64_t r = (int64_t)blockIdx.x * kRowWaves + wave; r < rows; r += step) {
+        const u32x4 *xr = x + r * nvec;
+        u32x4 v[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int c = lane + 64 * i;
+            v[i] = c < nvec ? xr[c] : u32x4{};
+        }
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) s += squares(v[i]);
+        const float rstd = 1.f / sqrtf(wave_sum(s) * inv_n + eps);
+        u32x4 *yr = y + r * nvec;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nvec) yr[c] = scaled(v[i], g[i], rstd);
+        }
+    }
+}
+
+// Longer rows: one pass for the sum of squares, a second to scale and store.
+__global__ void __launch_bounds__(kThreads)
+rmsnorm_stream_kernel(const u32x4 *x, const u32x4 *__restrict__ w,
+                      u32x4 *y, int64_t rows, int nvec, float inv_n, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t step = (int64_t)gridDim.x * kRowWaves;
+    for (int64_t r = (int64_t)blockIdx.x * kRowWaves + wave; r < rows; r += step) {
+        const u32x4 *xr = x + r * nvec;
+        float s = 0.f;
+        for (int c = lane; c < nvec; c += 64) s += squares(xr[c]);
+        const float rstd = 1.f / sqrtf(wave_sum(s) * inv_n + eps);
+        u32x4 *yr = y + r * nvec;
+        for (int c = lane; c < nvec; c += 64) yr[c] = scaled(xr[c], w[c], rstd);
+    }
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t p = (uintptr_t)a, q = (uintptr_t)b;
+    return p < q + nb && q < p + na;
+}
+
+}  // namespace
+
+extern "C" int tessera_rmsnorm_fwd(const void *x, const void *w, void *y, long long rows, int n,
+                                   float eps, void *stream) {
+    if (!x || !w || !y) return TESSERA_ERR_NULL;
+    if (rows < 1 || n < 8) return TESSERA_ERR_SHAPE;
+    if (n % 8 != 0 || n > kMaxN) return TESSERA_ERR_UNSUPPORTED;
+    if (!isfinite(eps) || eps < 0.f) return TESSERA_ERR_EPS;
+    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & 15u) return TESSERA_ERR_ALIGN;
+    if (rows > (1ll << 62) / n) return TESSERA_ERR_TOO_LARGE;
+    const size_t xbytes = (size_t)rows * n * 2, wbytes = (size_t)n * 2;
+    if ((y != x && overlaps(y, xbytes, x, xbytes)) || overlaps(y, xbytes, w, wbytes))
+        return TESSERA_ERR_ALIAS;
+
+    const int nvec = n / 8;
+    const int64_t groups = (rows + kRowWaves - 1) / kRowWaves;
+    const dim3 g((unsigned)(groups < kMaxGrid ? groups : kMaxGrid)), blk(kThreads);
+    hipStream_t s = (hipStream_t)stream;
+    const u32x4 *xv = (const u32x4 *)x, *wv = (const u32x4 *)w;
+    u32x4 *yv = (u32x4 *)y;
+    const float inv_n = 1.f / (float)n;
+    const int64_t nrows = rows;
+    if (nvec <= 64)
+        hipLaunchKernelGGL(rmsnorm_reg_kernel<1>, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
+                           eps);
+    else if (nvec <= 128)
+        hipLaunchKernelGGL(rmsnorm_reg_kernel<2>, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
+                           eps);
+    else if (nvec <= 256)
+        hipLaunchKernelGGL(rmsnorm_reg_kernel<4>, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
+                           eps);
+    else if (nvec <= 512)
+        hipLaunchKernelGGL(rmsnorm_reg_kernel<8>, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
+                           eps);
+    else if (nvec <= kRegMaxVec)
+        hipLaunchKernelGGL(rmsnorm_reg_kernel<16>, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
+                           eps);
+    else
+        hipLaunchKernelGGL(rmsnorm_stream_kernel, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
+                           eps);
+    return tessera_launch_status();
+}

@@ -119,6 +119,39 @@ KV_WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class RmsWorkload:
+    """Fused RMSNorm over `rows` token rows of `n` features (bf16)."""
+    name: str
+    rows: int
+    n: int
+    eps: float = 1e-6
+    seed: int = 0
+
+    @property
+    def bytes(self) -> float:
+        """HBM bytes a pass must move: x read and y written once, w read once."""
+        return 2.0 * (2 * self.rows * self.n + self.n)
+
+    def describe(self) -> str:
+        return f"rows={self.rows} n={self.n} bf16 eps={self.eps:g}"
+
+
+# The 16k tokens of the long-context workload at its model width, Hq * D = 4096.
+RMS_WORKLOADS = {
+    "rmsnorm_16384x4096": RmsWorkload("rmsnorm_16384x4096", 16384, 4096),
+}
+
+
+def make_rmsnorm(rows, n, seed=0, scale=1.0):
+    """x [rows, n] ~ scale * N(0,1) and w [n] ~ 1 + 0.5 * N(0,1), drawn in that
+    order with default_rng(seed) in float32, then cast to bf16 (nearest even)."""
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(rng.standard_normal((rows, n), dtype=np.float32) * np.float32(scale))
+    w = torch.from_numpy(1.0 + 0.5 * rng.standard_normal(n, dtype=np.float32))
+    return x.to(torch.bfloat16).contiguous(), w.to(torch.bfloat16).contiguous()
+
+
 def default_scale(D: int) -> float:
     """The fp32 value of 1/sqrt(D), returned as a Python float."""
     return float(np.float32(1.0 / math.sqrt(D)))

@@ -54,7 +54,8 @@ enum tessera_attn_status {
     TESSERA_ERR_ALIGN = 6,       /* q, k, v, out not 16-byte or lse not 4-byte aligned */
     TESSERA_ERR_ALIAS = 7,       /* out or lse overlaps an input or each other */
     TESSERA_ERR_TOO_LARGE = 8,   /* the launch grid would exceed 2^31 - 1 workgroups */
-    TESSERA_ERR_LAUNCH = 9       /* the HIP kernel launch failed */
+    TESSERA_ERR_LAUNCH = 9,      /* the HIP kernel launch failed */
+    TESSERA_ERR_EPS = 10         /* RMSNorm eps is NaN, infinite or negative */
 };
 
 /*

@@ -8,7 +8,7 @@ import pytest
 from attention_flashattention_fwd_amd import binding
 
 ROOT = Path(__file__).resolve().parent.parent
-HEADER = ROOT / "include" / "tessera_attn.h"
+HEADERS = sorted((ROOT / "include").glob("*.h"))
 
 # fake, well separated, 16-byte aligned device addresses: validation rejects
 # these calls before any HIP call is made, so they are never dereferenced
@@ -16,8 +16,11 @@ Q, K, V, O, L = (1 << 44), (2 << 44), (3 << 44), (4 << 44), (5 << 44)
 
 
 def declared_functions():
-    text = HEADER.read_text()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tessera_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tessera_\w+)\s*\(",
+                                h.read_text(), re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_exports():
@@ -32,7 +35,7 @@ def test_library_loads_and_exports_every_symbol():
 
 
 def test_status_strings():
-    for code in range(0, 10):
+    for code in range(0, 11):
         assert binding.status_string(code)
     assert binding.status_string(123) == "unknown status"
     assert binding.lib().tessera_attn_last_error() == b""
@@ -74,3 +77,48 @@ def test_binding_rejects_cpu_tensors():
     k = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         binding.attn_fwd(q, k, k)
+
+
+def call_kv(q=Q, k=K, v=V, o=O, l=L, B=1, Hq=4, Hkv=2, Tq=16, Tk=64, D=64, causal=1,
+            scale=0.125):
+    return binding.raw_fwd_kv(q, k, v, o, l, B, Hq, Hkv, Tq, Tk, D, causal, scale, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(k=None), binding.ERR_NULL),
+    (dict(Tq=0), binding.ERR_SHAPE),
+    (dict(Tk=0), binding.ERR_SHAPE),
+    (dict(Tq=65), binding.ERR_SHAPE),                 # causal with more query than key rows
+    (dict(D=96), binding.ERR_UNSUPPORTED),
+    (dict(causal=-1), binding.ERR_CAUSAL),
+    (dict(scale=float("nan")), binding.ERR_SCALE),
+    (dict(v=V + 4), binding.ERR_ALIGN),
+    (dict(o=K + 1024), binding.ERR_ALIAS),
+])
+def test_kv_bad_arguments_are_rejected_before_launch(kwargs, code):
+    assert call_kv(**kwargs) == code
+
+
+X, W, Y = (6 << 44), (7 << 44), (8 << 44)
+
+
+def call_rms(x=X, w=W, y=Y, rows=4, n=64, eps=1e-6):
+    return binding.raw_rmsnorm(x, w, y, rows, n, eps, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(x=None), binding.ERR_NULL),
+    (dict(w=None), binding.ERR_NULL),
+    (dict(rows=0), binding.ERR_SHAPE),
+    (dict(n=0), binding.ERR_SHAPE),
+    (dict(n=12), binding.ERR_UNSUPPORTED),
+    (dict(n=65544), binding.ERR_UNSUPPORTED),
+    (dict(eps=-1.0), binding.ERR_EPS),
+    (dict(eps=float("nan")), binding.ERR_EPS),
+    (dict(x=X + 8), binding.ERR_ALIGN),
+    (dict(y=X + 16), binding.ERR_ALIAS),              # partial overlap with x
+    (dict(y=W), binding.ERR_ALIAS),
+    (dict(rows=1 << 60, n=64), binding.ERR_TOO_LARGE),
+])
+def test_rmsnorm_bad_arguments_are_rejected_before_launch(kwargs, code):
+    assert call_rms(**kwargs) == code
