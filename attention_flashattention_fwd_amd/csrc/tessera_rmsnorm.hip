@@ -33,7 +33,7 @@ constexpr int kRowWaves = 4;                 // waves (rows in flight) per workg
 constexpr int kThreads = 64 * kRowWaves;
 constexpr int kMaxN = 65536;
 constexpr int kRegMaxVec = 1024;             // 16-byte pieces held in registers: n <= 8192
-constexpr int kMaxGrid = 4096;               // workgroups; waves stride over the rows
+constexpr int kMaxGrid = 16384;              // workgroups; waves stride over the rows
 
 // The two bf16 values of a 32-bit word, as fp32 (exact).
 __device__ __forceinline__ float lo_of(uint32_t u) { return __uint_as_float(u << 16); }

@@ -50,6 +50,8 @@ def parse_args(argv=None):
                    help="wall-time budget of the CPU-oracle baseline sample")
     p.add_argument("--no-secondary", action="store_true", help="skip the secondary workloads")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline (profiling runs)")
+    p.add_argument("--rmsnorm-only", action="store_true",
+                   help="only time the fused RMSNorm workload(s) (profiling runs)")
     p.add_argument("--hbm-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (to scale HBM counters)")
     p.add_argument("--gemm-calibration", action="store_true",
@@ -225,6 +227,37 @@ def main(argv=None):
                           "launches": max(1, args.steps) + args.warmup}))
         return 0
 
+    def rmsnorm_lines():
+        """The fused RMSNorm (HBM-bound): bytes moved per call over the kernel time."""
+        res = {}
+        for name, rw in inputs.RMS_WORKLOADS.items():
+            x, g = inputs.make_rmsnorm(rw.rows, rw.n, rw.seed)
+            xd, gd = x.to(dev), g.to(dev)
+            yd = torch.empty_like(xd)
+            torch.cuda.synchronize()
+            fn = lambda: binding.rmsnorm_fwd_into(xd, gd, yd, rw.eps, stream=stream)  # noqa: E731
+            r_ms, _, r_med, _ = time_steps(torch, fn, max(20, args.steps), args.warmup, stream,
+                                           warm_seconds=0.2)
+            gbs = rw.bytes / (r_ms * 1e-3) / 1e9
+            # context: a plain device copy of the same tensor (torch), what HBM gives a
+            # read-once / write-once pass on this part
+            c_ms, _, _, _ = time_steps(torch, lambda: yd.copy_(xd), max(20, args.steps),
+                                       args.warmup, stream, warm_seconds=0.1)
+            copy_gbs = 2.0 * xd.numel() * 2 / (c_ms * 1e-3) / 1e9
+            res[name] = {
+                "config": rw.describe(),
+                "us_per_call": round(r_ms * 1e3, 2),
+                "us_median": round(r_med * 1e3, 2),
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                             "device_copy_gbs": round(copy_gbs, 1)},
+            }
+        return res
+
+    if args.rmsnorm_only:
+        print(json.dumps(rmsnorm_lines()))
+        return 0
+
     def measure(name, steps, warmup, with_cpu, warm_seconds=0.0):
         if name in inputs.KV_WORKLOADS:   # Tq new rows against Tk cached rows
             w = inputs.KV_WORKLOADS[name]
@@ -276,30 +309,7 @@ def main(argv=None):
                                      / PEAK_BF16_TFLOPS, 2),
             }
 
-    # The fused RMSNorm (HBM-bound): bytes moved per call over the kernel time.
-    if not args.no_secondary:
-        for name, rw in inputs.RMS_WORKLOADS.items():
-            x, g = inputs.make_rmsnorm(rw.rows, rw.n, rw.seed)
-            xd, gd = x.to(dev), g.to(dev)
-            yd = torch.empty_like(xd)
-            torch.cuda.synchronize()
-            fn = lambda: binding.rmsnorm_fwd_into(xd, gd, yd, rw.eps, stream=stream)  # noqa: E731
-            r_ms, _, r_med, _ = time_steps(torch, fn, max(20, args.steps), args.warmup, stream,
-                                           warm_seconds=0.2)
-            gbs = rw.bytes / (r_ms * 1e-3) / 1e9
-            # context: a plain device copy of the same tensor (torch), what HBM gives a
-            # read-once / write-once pass on this part
-            c_ms, _, _, _ = time_steps(torch, lambda: yd.copy_(xd), max(20, args.steps),
-                                       args.warmup, stream, warm_seconds=0.1)
-            copy_gbs = 2.0 * xd.numel() * 2 / (c_ms * 1e-3) / 1e9
-            secondary[name] = {
-                "config": rw.describe(),
-                "us_per_call": round(r_ms * 1e3, 2),
-                "us_median": round(r_med * 1e3, 2),
-                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                             "device_copy_gbs": round(copy_gbs, 1)},
-            }
+    secondary.update(rmsnorm_lines() if not args.no_secondary else {})
 
     line = {
         "metric": "attention fwd TFLOP/s (causal-adjusted) and % of MI355X bf16 MFMA peak",
