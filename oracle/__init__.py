@@ -5,6 +5,7 @@ import this package.  The HIP library never uses it.
 """
 from .oracle import (  # noqa: F401
     OracleLib,
+    attn_bwd,
     attn_fwd,
     attn_fwd_kv,
     attn_probs,

@@ -19,6 +19,7 @@ import numpy as np
 HERE = Path(__file__).resolve().parent
 SOURCE = HERE / "attn_oracle.c"
 RMS_SOURCE = HERE / "rmsnorm_oracle.c"
+BWD_SOURCE = HERE / "attn_bwd_oracle.c"
 LIBRARY = HERE / "liboracle_attn.so"
 
 DTYPE_F32 = 0
@@ -28,10 +29,11 @@ _c_double_p = ctypes.POINTER(ctypes.c_double)
 _c_int64_p = ctypes.POINTER(ctypes.c_int64)
 
 
-def build(source: Path = SOURCE, output: Path = LIBRARY, rms_source: Path = RMS_SOURCE) -> Path:
+def build(source: Path = SOURCE, output: Path = LIBRARY, rms_source: Path = RMS_SOURCE,
+          bwd_source: Path = BWD_SOURCE) -> Path:
     """Compile the oracle with gcc (plain -O2, OpenMP) into a shared library."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-           str(source), str(rms_source), "-o", str(output) + ".tmp", "-lm"]
+           str(source), str(rms_source), str(bwd_source), "-o", str(output) + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(str(output) + ".tmp", output)
     return output
@@ -59,6 +61,10 @@ class OracleLib:
         lib.tessera_oracle_rmsnorm.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                                ctypes.c_int, ctypes.c_double, _c_double_p]
         lib.tessera_oracle_rmsnorm.restype = ctypes.c_int
+        vp, ci = ctypes.c_void_p, ctypes.c_int
+        lib.tessera_oracle_attn_bwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
+                                                ctypes.c_double] + [_c_double_p] * 4
+        lib.tessera_oracle_attn_bwd.restype = ctypes.c_int
         lib.tessera_oracle_threads.argtypes = [ctypes.c_int]
         lib.tessera_oracle_threads.restype = ctypes.c_int
         self.lib = lib
@@ -160,6 +166,25 @@ class OracleLib:
         self._check(rc, "tessera_oracle_rmsnorm")
         return y
 
+    def attn_bwd(self, q, k, v, dout, causal: bool, scale: float):
+        """Gradients of the attention forward for output gradient dout (all uint16
+        bf16 patterns; q, dout [B,Hq,T,D], k, v [B,Hkv,T,D]).  Returns dq, dk, dv
+        and Delta [B,Hq,T], fp64."""
+        (q, k, v), code, (B, Hq, Hkv, T, D) = self._prep(q, k, v)
+        dout = np.ascontiguousarray(dout)
+        if code != DTYPE_BF16 or dout.dtype != np.uint16 or dout.shape != q.shape:
+            raise ValueError("attn_bwd takes bf16 patterns, dout shaped like q")
+        dq = np.empty(q.shape, np.float64)
+        dk = np.empty(k.shape, np.float64)
+        dv = np.empty(v.shape, np.float64)
+        delta = np.empty((B, Hq, T), np.float64)
+        rc = self.lib.tessera_oracle_attn_bwd(
+            self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout), B, Hq, Hkv, T, D,
+            int(bool(causal)), float(scale), *(a.ctypes.data_as(_c_double_p)
+                                               for a in (dq, dk, dv, delta)))
+        self._check(rc, "tessera_oracle_attn_bwd")
+        return dq, dk, dv, delta
+
     def threads(self, nthreads: int = 0) -> int:
         return int(self.lib.tessera_oracle_threads(int(nthreads)))
 
@@ -171,7 +196,8 @@ def load() -> OracleLib:
     """The oracle built from attn_oracle.c (compiled on first use if absent)."""
     global _DEFAULT
     if _DEFAULT is None:
-        newest = max(SOURCE.stat().st_mtime, RMS_SOURCE.stat().st_mtime)
+        newest = max(SOURCE.stat().st_mtime, RMS_SOURCE.stat().st_mtime,
+                     BWD_SOURCE.stat().st_mtime)
         if not LIBRARY.exists() or LIBRARY.stat().st_mtime < newest:
             build()
         _DEFAULT = OracleLib(LIBRARY)
@@ -192,6 +218,10 @@ def attn_rows(q, k, v, causal, scale, rows, nthreads=0):
 
 def attn_probs(q, k, v, causal, scale):
     return load().attn_probs(q, k, v, causal, scale)
+
+
+def attn_bwd(q, k, v, dout, causal, scale):
+    return load().attn_bwd(q, k, v, dout, causal, scale)
 
 
 def rmsnorm(x, w, eps):

@@ -9,9 +9,10 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.oracle import RMS_SOURCE, SOURCE, OracleLib
+from oracle.oracle import BWD_SOURCE, RMS_SOURCE, SOURCE, OracleLib
 from tests import oracle_pins
 from tests.oracle_pins import ALL_PINS, rand_inputs
+from tests.attn_bwd_pins import ALL_BWD_PINS
 from tests.rmsnorm_pins import ALL_RMS_PINS
 
 
@@ -20,7 +21,7 @@ def lib():
     return oracle.load()
 
 
-@pytest.mark.parametrize("pin", ALL_PINS + ALL_RMS_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", ALL_PINS + ALL_RMS_PINS + ALL_BWD_PINS, ids=lambda f: f.__name__)
 def test_pin(lib, pin):
     pin(lib)
 
@@ -67,14 +68,41 @@ RMS_MUTANTS = {
 }
 
 
-def build_mutant(tmp_path: Path, attn_src: str, rms_src: str) -> OracleLib:
-    a, r = tmp_path / "mutant_attn.c", tmp_path / "mutant_rms.c"
+# The same for the backward oracle.
+BWD_MUTANTS = {
+    "delta_dropped": ("const double ds = s[j] * (dp[j] - dl);", "const double ds = s[j] * dp[j];"),
+    "ds_sign_flipped": ("const double ds = s[j] * (dp[j] - dl);",
+                        "const double ds = s[j] * (dl - dp[j]);"),
+    "dq_scale_dropped": ("dq[qi + d] += scale * ds *", "dq[qi + d] += ds *"),
+    "dk_from_keys": ("dk[kj + d] += scale * ds * wide(q, qi + d);",
+                     "dk[kj + d] += scale * ds * wide(k, kj + d);"),
+    "dv_from_ds": ("dv[kj + d] += s[j] * wide(dout, qi + d);",
+                   "dv[kj + d] += ds * wide(dout, qi + d);"),
+    "dp_from_keys": ("dot += wide(dout, qi + d) * wide(v,", "dot += wide(dout, qi + d) * wide(k,"),
+    "mask_ignored": ("const int n = causal ? i + 1 : T;", "const int n = T;"),
+    "unnormalised": ("s[j] /= Z;", "s[j] /= 1.0;"),
+}
+
+
+def build_mutant(tmp_path: Path, attn_src: str, rms_src: str, bwd_src: str = None) -> OracleLib:
+    a, r, w = tmp_path / "mutant_attn.c", tmp_path / "mutant_rms.c", tmp_path / "mutant_bwd.c"
     a.write_text(attn_src)
     r.write_text(rms_src)
+    w.write_text(bwd_src if bwd_src is not None else BWD_SOURCE.read_text())
     so = tmp_path / "libmutant.so"
     subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", str(a), str(r),
-                    "-o", str(so), "-lm"], check=True)
+                    str(w), "-o", str(so), "-lm"], check=True)
     return OracleLib(so)
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_planted_backward_mistake_is_caught(tmp_path: Path, name):
+    old, new = BWD_MUTANTS[name]
+    src = BWD_SOURCE.read_text()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutant = build_mutant(tmp_path, SOURCE.read_text(), RMS_SOURCE.read_text(),
+                          src.replace(old, new, 1))
+    assert caught_by(mutant, ALL_BWD_PINS), f"no pin rejects the planted mistake {name}"
 
 
 def caught_by(mutant, pins):
