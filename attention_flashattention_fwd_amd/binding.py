@@ -29,7 +29,7 @@ ERR_TOO_LARGE = 8
 ERR_LAUNCH = 9
 ERR_EPS = 10
 
-EXPORTS = ("tessera_attn_fwd", "tessera_attn_fwd_kv", "tessera_attn_fwd_f32",
+EXPORTS = ("tessera_attn_fwd", "tessera_attn_fwd_kv", "tessera_attn_fwd_f32", "tessera_attn_bwd",
            "tessera_attn_status_string", "tessera_attn_last_error", "tessera_attn_version",
            "tessera_rmsnorm_fwd")
 
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.tessera_attn_fwd_f32.restype = i
         L.tessera_attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
         L.tessera_attn_fwd_kv.restype = i
+        L.tessera_attn_bwd.argtypes = [vp] * 10 + [i] * 6 + [f, vp]
+        L.tessera_attn_bwd.restype = i
         L.tessera_rmsnorm_fwd.argtypes = [vp, vp, vp, ctypes.c_longlong, i, f, vp]
         L.tessera_rmsnorm_fwd.restype = i
         L.tessera_attn_status_string.argtypes = [i]
@@ -248,3 +250,47 @@ def rmsnorm_fwd(x, w, eps: float = RMSNORM_EPS):
     y = torch.empty_like(x)
     rmsnorm_fwd_into(x, w, y, eps)
     return y
+
+
+def raw_bwd(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, T, D, causal, scale,
+            stream) -> int:
+    """Call tessera_attn_bwd with integer device addresses; returns the status."""
+    return int(lib().tessera_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, delta, int(B),
+                                      int(Hq), int(Hkv), int(T), int(D), int(causal),
+                                      float(np.float32(scale)), stream))
+
+
+def attn_bwd(q, k, v, out, lse, dout, causal: bool = True, scale: float | None = None,
+             stream=None):
+    """Gradients of attn_fwd (bfloat16): given its inputs, its results out and
+    lse, and the output gradient dout, returns (dq, dk, dv, delta), delta
+    being the row sums of dout * out [B,Hq,T] float32."""
+    import torch
+
+    B, Hq, Hkv, T, D = _check_inputs(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("attn_bwd takes bfloat16 q, k, v")
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, Hq, T) or lse.dtype != torch.float32 or lse.device != q.device \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, T] on q's device")
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = raw_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                     delta.data_ptr(), B, Hq, Hkv, T, D, int(bool(causal)), scale, handle)
+    if st != OK:
+        msg = status_string(st)
+        if st == ERR_LAUNCH:
+            msg += ": " + lib().tessera_attn_last_error().decode()
+        raise RuntimeError(f"tessera_attn_bwd failed ({st}): {msg}")
+    return dq, dk, dv, delta

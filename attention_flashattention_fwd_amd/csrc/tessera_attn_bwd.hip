@@ -1,0 +1,553 @@
+// tessera_attn_bwd.hip -- gfx950 (MI355X) kernels and C ABI of the attention
+// backward pass: dq, dk, dv of the causal grouped-query attention forward for
+// an output gradient dO (the fused backward that the page "Tessera: a
+// from-scratch distillation and serving stack in one repository", section
+// "The kernel set and its torch fallback", lists as missing).
+//
+// With P the forward's softmax weights, rebuilt from the forward's lse:
+//     P_ij  = exp(scale q_i.k_j - lse_i)          dP_ij = dO_i . v_j
+//     Delta_i = sum_d dO_id O_id                   dS_ij = P_ij (dP_ij - Delta_i)
+//     dq_i = scale sum_j dS_ij k_j    dk_j = scale sum_i dS_ij q_i    dv_j = sum_i P_ij dO_i
+// (dk and dv also summed over the query heads of a KV head's group).
+//
+// Two kernels, each owning what it accumulates, so no atomics and the result
+// does not depend on scheduling:
+//   * attn_bwd_dq_kernel: a workgroup per query tile (as in the forward); it
+//     streams K and V tiles, forms S^T = K Q^T and dP^T = V dO^T on the
+//     matrix cores, P and dS on the vector ALUs, and dq^T += K^T dS^T.  It
+//     also writes Delta, from the dO and O rows it holds.
+//   * attn_bwd_dkdv_kernel: a workgroup per 128-key tile of one KV head; it
+//     streams the Q and dO tiles of every query head of the group, forms
+//     S = Q K^T and dP = dO V^T, and accumulates dv^T += dO^T P and
+//     dk^T += Q^T dS.
+// Both use v_mfma_f32_32x32x16_bf16 in the transposed form of the forward:
+// the stationary operand (Q and dO, or K and V) sits in registers as the B
+// operand, streamed tiles are read from LDS row by row (A operand of the
+// score-like products) or through ds_read_b64_tr_b16 (A operand of the
+// accumulating products), and the P / dS fragments a lane computes are
+// already the B operand of the accumulating products.  Tiles are double
+// buffered in LDS through registers; P and dS are rounded to bf16 for the
+// matrix cores, everything else is fp32.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "tessera_attn.h"
+
+int tessera_launch_status(void);   // tessera_attn.hip
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.442695040888963407f;
+constexpr int kTileRows = 64;    // rows of a streamed tile
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte chunk swizzle of a D-wide bf16 row in LDS (keeps the row reads of
+// the MFMA A operand on distinct banks).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return row & 15;
+    else if constexpr (D == 64) return (row >> 1) & 7;
+    else return (row >> 2) & 3;
+}
+
+// A streamed tile: kTileRows rows of D bf16 values, row-major with swizzled
+// chunks.
+template <int D>
+struct Tile {
+    static constexpr int kBytes = kTileRows * D * 2;
+    static constexpr int kChunks = kTileRows * D / 8;
+};
+
+// Per-lane LDS byte offsets of the two A-operand reads of a tile.
+//  * row read, block b (rows 32b .. 32b+31), step ks: lane (col, hi) reads 16
+//    bytes of row 32b + col, dims 16 ks + 8 hi .. +7.  The swizzle of row
+//    col + 32 equals that of row col, so block 1 is a fixed +32 rows.
+//  * transposed read (X^T as the A operand, K dimension = rows): for step st
+//    and dim block db, lane (grp, s16) reads 8 bytes of rows
+//    16 st + 4 hi + s16/4 and that + 8, dims 32 db + 16 (grp & 1) + 4 (s16 & 3)
+//    .. +3; after ds_read_b64_tr_b16 it holds rows {4hi..4hi+3, 8+4hi..8+4hi+3}
+//    of one dim, the order of a lane's rows in an MFMA result, so a P or dS
+//    fragment is the matching B operand as it stands.  st is a fixed offset.
+template <int D>
+struct TileOffsets {
+    uint32_t row[D / 16];
+    uint32_t tr[D / 32][2];
+    __device__ __forceinline__ explicit TileOffsets(int lane) {
+        constexpr int kRowBytes = D * 2;
+        const int col = lane & 31, hi = lane >> 5, grp = lane >> 4, s16 = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            row[ks] = col * kRowBytes + (((2 * ks + hi) ^ swz<D>(col)) << 4);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int d = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = 4 * hi + (s16 >> 2) + 8 * h;
+                tr[db][h] = r * kRowBytes + (((d >> 3) ^ swz<D>(r)) << 4) + (d & 7) * 2;
+            }
+        }
+    }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 read_row(const LDS_AS char *tile, const TileOffsets<D> &o,
+                                           int block, int ks) {
+    return *(const LDS_AS bf16x8 *)(tile + o.row[ks] + block * 32 * D * 2);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr(const LDS_AS char *tile, const TileOffsets<D> &o,
+                                          int st, int db) {
+    const LDS_AS char *base = tile + st * 16 * D * 2;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(base + o.tr[db][0]));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(base + o.tr[db][1]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Global -> register -> LDS staging of kTileRows rows of one [T, D] head,
+// spread over NT threads.  Rows at or past `rows` are written as zeros.
+template <int D, int NT>
+struct TileStager {
+    static constexpr int kPer = (Tile<D>::kChunks + NT - 1) / NT;
+    u32x4 r[kPer];
+    __device__ __forceinline__ void fetch(const uint16_t *head, int row0, int rows, int tid) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + NT * i;
+            const int row = c / (D / 8), ch = c % (D / 8);
+            const bool ok = (Tile<D>::kChunks % NT == 0 || c < Tile<D>::kChunks) &&
+                            row0 + row < rows;
+            r[i] = ok ? *(const u32x4 *)(head + (int64_t)(row0 + row) * D + 8 * ch) : u32x4{};
+        }
+    }
+    __device__ __forceinline__ void store(LDS_AS char *tile, int tid) const {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + NT * i;
+            if (Tile<D>::kChunks % NT != 0 && c >= Tile<D>::kChunks) continue;
+            const int row = c / (D / 8), ch = c % (D / 8);
+            *(LDS_AS u32x4 *)(tile + row * D * 2 + ((ch ^ swz<D>(row)) << 4)) = r[i];
+        }
+    }
+};
+
+// The B-operand fragment of a stationary [32 rows, D] block: lane (col, hi)
+// holds 8 values of row min(row0 + col, rows - 1), dims 16 ks + 8 hi .. +7.
+template <int D>
+__device__ __forceinline__ void load_fragment(bf16x8 (&f)[D / 16], const uint16_t *head,
+                                              int row0, int rows, int lane) {
+    const int row = min(row0 + (lane & 31), rows - 1);
+    const uint16_t *src = head + (int64_t)row * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) f[ks] = *(const bf16x8 *)(src + 16 * ks);
+}
+
+// Packs two f32x16 MFMA results (rows 0-31 and 32-63 of a 64-row step
+// sequence) into the four bf16 B-operand words per 16-row step.
+__device__ __forceinline__ void pack_steps(u32x4 (&out)[4], const f32x16 &a, const f32x16 &b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bf16x2 p0 = __builtin_convertvector((f32x2){a[2 * e], a[2 * e + 1]}, bf16x2);
+        const bf16x2 p1 = __builtin_convertvector((f32x2){b[2 * e], b[2 * e + 1]}, bf16x2);
+        out[e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p0);
+        out[2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
+    }
+}
+
+// Writes a [D, 32] accumulator (lane: column col of its 32, dims of every
+// block) times `mul` as bf16 row `row` of a [rows, D] tensor.
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t *dst_row, const f32x16 (&acc)[D / 32],
+                                           float mul, int hi) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g4 + e] * mul;
+            *(bf16x4 *)(dst_row + 32 * db + 8 * g4 + 4 * hi) = __builtin_convertvector(x, bf16x4);
+        }
+    }
+}
+
+struct BwdArgs {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;
+    uint16_t *dq, *dk, *dv;
+    float *delta;
+    int Hq, Hkv, T, G;
+    int hg, nqb, nslots, nbh, nqt;   // dq kernel work split (as in the forward)
+    int dq_waves;
+    int nkt;                         // 128-key tiles per head (dk/dv kernel)
+    int causal;
+    float scale;
+    float c;                         // scale * log2(e)
+};
+
+// ---------------------------------------------------------------------------
+// dq (and Delta): a workgroup of NW waves per query tile of 32 * nqb rows and
+// hg query heads of one KV head; wave w takes head w % hg and query block
+// w / hg, as in the forward.  D = 128 needs more than 256 registers per
+// wave, so it runs 4 waves (one per SIMD, up to 512 each); smaller D run 8.
+// ---------------------------------------------------------------------------
+template <int D>
+constexpr int kDqWaves = D == 128 ? 4 : 8;
+
+template <int D, int NW = kDqWaves<D>>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+attn_bwd_dq_kernel(BwdArgs a) {
+    constexpr int kDqThreads = 64 * NW;
+    __shared__ __attribute__((aligned(16))) char lds_k[2][Tile<D>::kBytes];
+    __shared__ __attribute__((aligned(16))) char lds_v[2][Tile<D>::kBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5, col = lane & 31;
+
+    const int per_tile = a.nbh * a.nslots;
+    const int qt_rev = blockIdx.x / per_tile;
+    const int rem = blockIdx.x - qt_rev * per_tile;
+    const int qt = a.causal ? (a.nqt - 1 - qt_rev) : qt_rev;
+    const int slot = rem / a.nbh;
+    const int bh = rem - slot * a.nbh;
+    const int b = bh / a.Hkv;
+    const int head = (bh - b * a.Hkv) * a.G + slot * a.hg + (w % a.hg);
+    const int rows_wg = 32 * a.nqb;
+    const int q0 = qt * rows_wg;
+    const int qw0 = q0 + 32 * (w / a.hg);
+    const int query = qw0 + col;
+    const int T = a.T;
+    const bool causal = a.causal != 0;
+
+    const int64_t qhead = ((int64_t)b * a.Hq + head) * T;   // row index of (b, head, 0)
+    const uint16_t *khead = a.k + (int64_t)bh * T * D;
+    const uint16_t *vhead = a.v + (int64_t)bh * T * D;
+
+    const int q_end = min(q0 + rows_wg, T);
+    const int ntiles = ((causal ? q_end : T) + kTileRows - 1) / kTileRows;
+
+    TileStager<D, kDqThreads> ks_, vs_;
+    ks_.fetch(khead, 0, T, tid);
+    vs_.fetch(vhead, 0, T, tid);
+
+    // Stationary fragments, lse and Delta of this lane's query row.
+    bf16x8 qf[D / 16], dof[D / 16], of[D / 16];
+    load_fragment<D>(qf, a.q + qhead * D, qw0, T, lane);
+    load_fragment<D>(dof, a.dout + qhead * D, qw0, T, lane);
+    load_fragment<D>(of, a.o + qhead * D, qw0, T, lane);
+    float dl = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dl += (float)dof[ks][e] * (float)of[ks][e];
+    }
+    dl += __shfl_xor(dl, 32);                    // the other half of the row's dims
+    const int qrow = min(query, T - 1);
+    const float lse2 = a.lse[qhead + qrow] * kLog2e;
+    if (hi == 0 && query < T) a.delta[qhead + query] = dl;
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    const TileOffsets<D> off(lane);
+    const float c = a.c;
+
+    ks_.store((LDS_AS char *)lds_k[0], tid);
+    vs_.store((LDS_AS char *)lds_v[0], tid);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int cur = t & 1;
+        if (t + 1 < ntiles) {
+            ks_.fetch(khead, (t + 1) * kTileRows, T, tid);
+            vs_.fetch(vhead, (t + 1) * kTileRows, T, tid);
+        }
+        const LDS_AS char *kt = (const LDS_AS char *)lds_k[cur];
+        const LDS_AS char *vt = (const LDS_AS char *)lds_v[cur];
+        f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            s0 = mfma32(read_row<D>(kt, off, 0, ks), qf[ks], s0);
+            s1 = mfma32(read_row<D>(kt, off, 1, ks), qf[ks], s1);
+            p0 = mfma32(read_row<D>(vt, off, 0, ks), dof[ks], p0);
+            p1 = mfma32(read_row<D>(vt, off, 1, ks), dof[ks], p1);
+        }
+        // exponent of P; keys hidden from this query (causal) or past T get -inf
+        const int j0 = t * kTileRows;
+        f32x16 x0, x1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            x0[i] = __builtin_fmaf(s0[i], c, -lse2);
+            x1[i] = __builtin_fmaf(s1[i], c, -lse2);
+        }
+        if (j0 + kTileRows > T || (causal && j0 + kTileRows - 1 > qw0)) {
+            const int last = (causal ? qrow : T - 1) - j0 - 4 * hi;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 8 * (i >> 2) + (i & 3);
+                if (r > last) x0[i] = -INFINITY;
+                if (r + 32 > last) x1[i] = -INFINITY;
+            }
+        }
+        f32x16 d0, d1;   // dS
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            d0[i] = __builtin_amdgcn_exp2f(x0[i]) * (p0[i] - dl);
+            d1[i] = __builtin_amdgcn_exp2f(x1[i]) * (p1[i] - dl);
+        }
+        u32x4 dsu[4];
+        pack_steps(dsu, d0, d1);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                acc[db] = mfma32(read_tr<D>(kt, off, st, db), __builtin_bit_cast(bf16x8, dsu[st]),
+                                 acc[db]);
+        }
+        if (t + 1 < ntiles) {
+            ks_.store((LDS_AS char *)lds_k[cur ^ 1], tid);
+            vs_.store((LDS_AS char *)lds_v[cur ^ 1], tid);
+        }
+        __syncthreads();
+    }
+    if (query < T) store_rows<D>(a.dq + (qhead + query) * D, acc, a.scale, hi);
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv: a workgroup of 4 waves (one per SIMD, up to 512 registers each) per
+// 128-key tile of one KV head; wave w owns keys k0 + 32 w .. +31.  It loops
+// over the query heads of the group and, for each, over the 64-row query
+// tiles that can see these keys.
+// ---------------------------------------------------------------------------
+constexpr int kKvWaves = 4;
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKeyTile = 32 * kKvWaves;
+
+template <int D>
+__global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_bwd_dkdv_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds_q[2][Tile<D>::kBytes];
+    __shared__ __attribute__((aligned(16))) char lds_d[2][Tile<D>::kBytes];
+    __shared__ __attribute__((aligned(16))) float lds_l[2][kTileRows];   // lse * log2 e
+    __shared__ __attribute__((aligned(16))) float lds_m[2][kTileRows];   // Delta
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5, col = lane & 31;
+
+    // key tile 0 first: under the causal mask it has the most query rows after it
+    const int kt_idx = (int)(blockIdx.x / a.nbh);
+    const int bh = blockIdx.x - kt_idx * a.nbh;
+    const int b = bh / a.Hkv;
+    const int hkv = bh - b * a.Hkv;
+    const int T = a.T;
+    const bool causal = a.causal != 0;
+    const int k0 = kt_idx * kKeyTile;
+    const int kw0 = k0 + 32 * w;
+    const int key = kw0 + col;
+
+    const uint16_t *khead = a.k + (int64_t)bh * T * D;
+    const uint16_t *vhead = a.v + (int64_t)bh * T * D;
+    bf16x8 kf[D / 16], vf[D / 16];
+    load_fragment<D>(kf, khead, kw0, T, lane);
+    load_fragment<D>(vf, vhead, kw0, T, lane);
+
+    f32x16 adk[D / 32], adv[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        adk[db] = f32x16{};
+        adv[db] = f32x16{};
+    }
+    const TileOffsets<D> off(lane);
+    const float c = a.c;
+
+    // the (head, query tile) sequence: heads of the group, tiles from the
+    // first that reaches these keys
+    const int qt_first = causal ? k0 / kTileRows : 0;
+    const int nq = (T + kTileRows - 1) / kTileRows;
+    const int per_head = nq - qt_first;
+    const int nsteps = a.G * per_head;
+    const int64_t head0 = (int64_t)b * a.Hq + (int64_t)hkv * a.G;   // first query head
+
+    TileStager<D, kKvThreads> qs_, ds_;
+    float l_in = 0.f, m_in = 0.f;
+    auto fetch = [&](int step) __attribute__((always_inline)) {
+        const int g = step / per_head, q0 = (qt_first + step % per_head) * kTileRows;
+        const int64_t hrow = (head0 + g) * T;
+        qs_.fetch(a.q + hrow * D, q0, T, tid);
+        ds_.fetch(a.dout + hrow * D, q0, T, tid);
+        if (tid < kTileRows) {
+            const bool ok = q0 + tid < T;
+            l_in = ok ? a.lse[hrow + q0 + tid] * kLog2e : INFINITY;   // P = 0 past T
+            m_in = ok ? a.delta[hrow + q0 + tid] : 0.f;
+        }
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
+        qs_.store((LDS_AS char *)lds_q[buf], tid);
+        ds_.store((LDS_AS char *)lds_d[buf], tid);
+        if (tid < kTileRows) {
+            lds_l[buf][tid] = l_in;
+            lds_m[buf][tid] = m_in;
+        }
+    };
+
+    fetch(0);
+    store(0);
+    __syncthreads();
+    for (int step = 0; step < nsteps; ++step) {
+        const int cur = step & 1;
+        if (step + 1 < nsteps) fetch(step + 1);
+        const int q0 = (qt_first + step % per_head) * kTileRows;
+        const LDS_AS char *qt = (const LDS_AS char *)lds_q[cur];
+        const LDS_AS char *dt = (const LDS_AS char *)lds_d[cur];
+        f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            s0 = mfma32(read_row<D>(qt, off, 0, ks), kf[ks], s0);
+            s1 = mfma32(read_row<D>(qt, off, 1, ks), kf[ks], s1);
+            p0 = mfma32(read_row<D>(dt, off, 0, ks), vf[ks], p0);
+            p1 = mfma32(read_row<D>(dt, off, 1, ks), vf[ks], p1);
+        }
+        // Lane: key column `key`; register i of block bl holds query row
+        // q0 + 32 bl + 8 (i / 4) + 4 hi + i % 4.
+        const bool need_mask = causal && q0 < kw0 + 31;
+        f32x16 e0, e1, d0, d1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 8 * j + 4 * hi;
+            const f32x4 la = *(const LDS_AS f32x4 *)&lds_l[cur][r];
+            const f32x4 lb = *(const LDS_AS f32x4 *)&lds_l[cur][r + 32];
+            const f32x4 ma = *(const LDS_AS f32x4 *)&lds_m[cur][r];
+            const f32x4 mb = *(const LDS_AS f32x4 *)&lds_m[cur][r + 32];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = 4 * j + u;
+                float xa = __builtin_fmaf(s0[i], c, -la[u]);
+                float xb = __builtin_fmaf(s1[i], c, -lb[u]);
+                if (need_mask) {
+                    if (q0 + r + u < key) xa = -INFINITY;
+                    if (q0 + 32 + r + u < key) xb = -INFINITY;
+                }
+                e0[i] = __builtin_amdgcn_exp2f(xa);
+                e1[i] = __builtin_amdgcn_exp2f(xb);
+                d0[i] = e0[i] * (p0[i] - ma[u]);
+                d1[i] = e1[i] * (p1[i] - mb[u]);
+            }
+        }
+        u32x4 pu[4], dsu[4];
+        pack_steps(pu, e0, e1);
+        pack_steps(dsu, d0, d1);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                adv[db] = mfma32(read_tr<D>(dt, off, st, db), __builtin_bit_cast(bf16x8, pu[st]),
+                                 adv[db]);
+                adk[db] = mfma32(read_tr<D>(qt, off, st, db), __builtin_bit_cast(bf16x8, dsu[st]),
+                                 adk[db]);
+            }
+        }
+        if (step + 1 < nsteps) store(cur ^ 1);
+        __syncthreads();
+    }
+    if (key < T) {
+        store_rows<D>(a.dk + ((int64_t)bh * T + key) * D, adk, a.scale, hi);
+        store_rows<D>(a.dv + ((int64_t)bh * T + key) * D, adv, 1.f, hi);
+    }
+}
+
+bool overlaps(const void *x, size_t nx, const void *y, size_t ny) {
+    const uintptr_t p = (uintptr_t)x, q = (uintptr_t)y;
+    return p < q + ny && q < p + nx;
+}
+
+}  // namespace
+
+extern "C" int tessera_attn_bwd(const void *q, const void *k, const void *v, const void *out,
+                                const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                                float *delta, int B, int Hq, int Hkv, int T, int D, int causal,
+                                float scale, void *stream) {
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta)
+        return TESSERA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || Hq % Hkv != 0) return TESSERA_ERR_SHAPE;
+    if (D != 32 && D != 64 && D != 128) return TESSERA_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return TESSERA_ERR_CAUSAL;
+    if (!isfinite(scale)) return TESSERA_ERR_SCALE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout |
+         (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
+        return TESSERA_ERR_ALIGN;
+    if (((uintptr_t)lse | (uintptr_t)delta) & 3u) return TESSERA_ERR_ALIGN;
+    const size_t qb = (size_t)B * Hq * T * D * 2, kb = (size_t)B * Hkv * T * D * 2;
+    const size_t lb = (size_t)B * Hq * T * 4;
+    const void *ins[6] = {q, k, v, out, dout, lse};
+    const size_t insz[6] = {qb, kb, kb, qb, qb, lb};
+    void *outs[4] = {dq, dk, dv, delta};
+    const size_t outsz[4] = {qb, kb, kb, lb};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return TESSERA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return TESSERA_ERR_ALIAS;
+    }
+
+    BwdArgs a;
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.o = (const uint16_t *)out;
+    a.dout = (const uint16_t *)dout;
+    a.lse = lse;
+    a.dq = (uint16_t *)dq;
+    a.dk = (uint16_t *)dk;
+    a.dv = (uint16_t *)dv;
+    a.delta = delta;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.T = T;
+    a.G = Hq / Hkv;
+    a.dq_waves = D == 128 ? kDqWaves<128> : kDqWaves<64>;
+    a.hg = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
+    a.nqb = a.dq_waves / a.hg;
+    a.nslots = a.G / a.hg;
+    a.nbh = B * Hkv;
+    a.nqt = (T + 32 * a.nqb - 1) / (32 * a.nqb);
+    a.nkt = (T + kKeyTile - 1) / kKeyTile;
+    a.causal = causal;
+    a.scale = scale;
+    a.c = scale * kLog2e;
+    const int64_t grid_dq = (int64_t)a.nqt * a.nbh * a.nslots;
+    const int64_t grid_kv = (int64_t)a.nkt * a.nbh;
+    if (grid_dq > 0x7fffffff || grid_kv > 0x7fffffff) return TESSERA_ERR_TOO_LARGE;
+
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 g1((unsigned)grid_dq), b1(64 * a.dq_waves), g2((unsigned)grid_kv), b2(kKvThreads);
+    // dq first: it writes the Delta rows the dk/dv kernel reads.
+    if (D == 128) {
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, g1, b1, 0, s, a);
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, g2, b2, 0, s, a);
+    } else if (D == 64) {
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, g1, b1, 0, s, a);
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, g2, b2, 0, s, a);
+    } else {
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<32>, g1, b1, 0, s, a);
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<32>, g2, b2, 0, s, a);
+    }
+    return tessera_launch_status();
+}

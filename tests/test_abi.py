@@ -122,3 +122,30 @@ def call_rms(x=X, w=W, y=Y, rows=4, n=64, eps=1e-6):
 ])
 def test_rmsnorm_bad_arguments_are_rejected_before_launch(kwargs, code):
     assert call_rms(**kwargs) == code
+
+
+DO, DQ, DK, DV, DL = (9 << 44), (10 << 44), (11 << 44), (12 << 44), (13 << 44)
+
+
+def call_bwd(q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, dl=DL, B=1, Hq=4, Hkv=2,
+             T=64, D=64, causal=1, scale=0.125):
+    return binding.raw_bwd(q, k, v, o, do, l, dq, dk, dv, dl, B, Hq, Hkv, T, D, causal, scale,
+                           None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(do=None), binding.ERR_NULL),
+    (dict(dl=None), binding.ERR_NULL),
+    (dict(T=0), binding.ERR_SHAPE),
+    (dict(Hq=3), binding.ERR_SHAPE),
+    (dict(D=80), binding.ERR_UNSUPPORTED),
+    (dict(causal=3), binding.ERR_CAUSAL),
+    (dict(scale=float("inf")), binding.ERR_SCALE),
+    (dict(dk=DK + 8), binding.ERR_ALIGN),
+    (dict(dl=DL + 2), binding.ERR_ALIGN),
+    (dict(dq=Q), binding.ERR_ALIAS),                # an output over an input
+    (dict(dv=DK + 64), binding.ERR_ALIAS),          # two outputs overlapping
+    (dict(dl=DO), binding.ERR_ALIAS),
+])
+def test_bwd_bad_arguments_are_rejected_before_launch(kwargs, code):
+    assert call_bwd(**kwargs) == code
