@@ -36,6 +36,7 @@ PEAK_BF16_TFLOPS = 2516.6     # dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GH
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "t16384_d128"
 SECONDARY = ["t4096_outliers", "t2048", "t2048_full", "chunk2048_t16384_d128"]
+BACKWARD = ["t16384_d128", "t4096_outliers"]
 KERNEL_SOURCE = ROOT / "attention_flashattention_fwd_amd" / "csrc" / "tessera_attn.hip"
 TRAFFIC_SUMMARY = ROOT / "profiles" / "hbm_traffic_attn_fwd_bf16_t16384_d128.md"
 
@@ -50,6 +51,8 @@ def parse_args(argv=None):
                    help="wall-time budget of the CPU-oracle baseline sample")
     p.add_argument("--no-secondary", action="store_true", help="skip the secondary workloads")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline (profiling runs)")
+    p.add_argument("--backward-only", action="store_true",
+                   help="only time the attention backward workload(s) (profiling runs)")
     p.add_argument("--rmsnorm-only", action="store_true",
                    help="only time the fused RMSNorm workload(s) (profiling runs)")
     p.add_argument("--hbm-calibration", action="store_true",
@@ -258,6 +261,36 @@ def main(argv=None):
         print(json.dumps(rmsnorm_lines()))
         return 0
 
+    def backward_lines():
+        """The attention backward on the long-context workload.  Rate counted the
+        usual way, 2.5x the forward's flops (the five products S, dP, dq, dk, dv);
+        the two kernels here execute seven (S and dP once in each)."""
+        res = {}
+        for name in BACKWARD:
+            w = inputs.WORKLOADS[name]
+            q, k, v = inputs.make_workload(w)
+            g = torch.Generator().manual_seed(7)
+            do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+            qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+            out, lse = binding.attn_fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+            fn = lambda: binding.attn_bwd(qd, kd, vd, out, lse, dod, w.causal,  # noqa: E731
+                                          w.scale, stream=stream)
+            b_ms, _, b_med, _ = time_steps(torch, fn, max(5, args.steps // 5), args.warmup,
+                                           stream, warm_seconds=0.2)
+            tf = 2.5 * w.flops / (b_ms * 1e-3) / 1e12
+            res[f"bwd_{name}"] = {
+                "config": w.describe() + ", backward (dq, dk, dv)",
+                "us_per_call": round(b_ms * 1e3, 2),
+                "us_median": round(b_med * 1e3, 2),
+                "tflops": round(tf, 1),
+                "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            }
+        return res
+
+    if args.backward_only:
+        print(json.dumps(backward_lines()))
+        return 0
+
     def measure(name, steps, warmup, with_cpu, warm_seconds=0.0):
         if name in inputs.KV_WORKLOADS:   # Tq new rows against Tk cached rows
             w = inputs.KV_WORKLOADS[name]
@@ -310,6 +343,7 @@ def main(argv=None):
             }
 
     secondary.update(rmsnorm_lines() if not args.no_secondary else {})
+    secondary.update(backward_lines() if not args.no_secondary else {})
 
     line = {
         "metric": "attention fwd TFLOP/s (causal-adjusted) and % of MI355X bf16 MFMA peak",
