@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the attention forward workloads.
+"""Seeded synthetic inputs for the attention workloads (forward, continuation,
+paged decode, backward) and the RMSNorm workload.
 
 This module only draws and casts random numbers; it holds none of the
 attention arithmetic, so both the HIP path's tests and the oracle may use it.
@@ -141,6 +142,107 @@ class RmsWorkload:
 RMS_WORKLOADS = {
     "rmsnorm_16384x4096": RmsWorkload("rmsnorm_16384x4096", 16384, 4096),
 }
+
+
+@dataclass(frozen=True)
+class PagedWorkload:
+    """Decoding Tq new tokens for each of B sequences whose keys and values sit
+    in a block-paged cache.  Cached lengths (the new tokens included) are drawn
+    uniformly from [ctx_min, ctx_max]; the physical blocks of all sequences are
+    a random permutation of the pool, `spare` blocks of which stay unused."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Tq: int
+    D: int
+    block_size: int
+    ctx_min: int
+    ctx_max: int
+    causal: bool = True
+    spare: int = 64
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.D)
+
+    @property
+    def max_blocks(self) -> int:
+        return -(-self.ctx_max // self.block_size)
+
+    def describe(self) -> str:
+        return (f"B={self.B} Hq={self.Hq} Hkv={self.Hkv} Tq={self.Tq} D={self.D} "
+                f"block_size={self.block_size} context {self.ctx_min}..{self.ctx_max} bf16 "
+                f"causal={int(self.causal)}")
+
+
+# Decode steps of a serving batch at the long-context head shape: 64 sequences
+# with 512 to 16384 cached tokens each, 16-token blocks.
+PAGED_WORKLOADS = {
+    "decode_b64_ctx16k_d128": PagedWorkload("decode_b64_ctx16k_d128", 64, 32, 8, 1, 128, 16,
+                                            512, 16384),
+}
+
+
+def paged_bytes(context_lens, Hq, Hkv, Tq, D, block_size) -> float:
+    """HBM bytes one decode call must move: every cached K and V row of every
+    sequence once, q read, out and lse written, and the block-table entries
+    in use read once (plus the length of each sequence)."""
+    n = np.asarray(context_lens, dtype=np.int64)
+    B = n.shape[0]
+    kv = 2.0 * 2 * Hkv * D * float(n.sum())
+    qo = 2.0 * 2 * B * Hq * Tq * D + 4.0 * B * Hq * Tq
+    table = 4.0 * float((-(-n // block_size)).sum()) + 4.0 * B
+    return kv + qo + table
+
+
+def make_paged(B, Hq, Hkv, Tq, D, block_size, context_lens=None, ctx_range=None, spare=64,
+               max_blocks=None, seed=0):
+    """Inputs of one paged decode call, as CPU tensors:
+    (q [B,Hq,Tq,D] bf16, k_cache, v_cache [num_blocks,Hkv,block_size,D] bf16,
+    block_table [B,max_blocks] int32, context_lens [B] int32).
+
+    Recipe, with default_rng(seed): the lengths (given, or drawn with
+    integers(lo, hi + 1, size=B) from ctx_range = (lo, hi)); then a permutation
+    of the num_blocks = used + spare physical blocks, whose first `used`
+    entries go to the logical blocks of sequence 0, 1, ... in order; then
+    standard_normal float32 draws of q, the K cache and the V cache, cast to
+    bf16 (nearest even).  Table entries past a sequence's last block are -1."""
+    rng = np.random.default_rng(seed)
+    if context_lens is None:
+        lo, hi = ctx_range
+        context_lens = rng.integers(lo, hi + 1, size=B)
+    lens = np.asarray(context_lens, dtype=np.int64)
+    if lens.shape != (B,) or (lens < 0).any():
+        raise ValueError("context_lens must be B non-negative lengths")
+    nblk = -(-lens // block_size)
+    if max_blocks is None:
+        max_blocks = max(1, int(nblk.max()))
+    if (nblk > max_blocks).any():
+        raise ValueError("a sequence needs more blocks than max_blocks")
+    used = int(nblk.sum())
+    num_blocks = used + spare
+    if num_blocks < 1:
+        raise ValueError("the cache needs at least one block")
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    at = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[at:at + nblk[b]]
+        at += int(nblk[b])
+    q = rng.standard_normal((B, Hq, Tq, D), dtype=np.float32)
+    kc = rng.standard_normal((num_blocks, Hkv, block_size, D), dtype=np.float32)
+    vc = rng.standard_normal((num_blocks, Hkv, block_size, D), dtype=np.float32)
+    bf = [torch.from_numpy(a).to(torch.bfloat16).contiguous() for a in (q, kc, vc)]
+    return (bf[0], bf[1], bf[2], torch.from_numpy(table),
+            torch.from_numpy(lens.astype(np.int32)))
+
+
+def make_paged_workload(w: PagedWorkload):
+    return make_paged(w.B, w.Hq, w.Hkv, w.Tq, w.D, w.block_size,
+                      ctx_range=(w.ctx_min, w.ctx_max), spare=w.spare,
+                      max_blocks=w.max_blocks, seed=w.seed)
 
 
 def make_rmsnorm(rows, n, seed=0, scale=1.0):

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for causal grouped-query attention (test infrastructure only).
+"""fp64 CPU oracle for the attention path (test infrastructure only).
 
 Only the tests, the package smoke check and the bench's CPU-baseline leg may
 import this package.  The HIP library never uses it.
@@ -12,6 +12,7 @@ from .oracle import (  # noqa: F401
     attn_rows,
     build,
     load,
+    paged_decode,
     rmsnorm,
     threads,
 )

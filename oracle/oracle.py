@@ -1,4 +1,5 @@
-"""ctypes wrapper around the plain-C fp64 attention oracle (attn_oracle.c).
+"""ctypes wrapper around the plain-C fp64 oracle (attn_oracle.c, rmsnorm_oracle.c,
+attn_bwd_oracle.c, paged_oracle.c).
 
 TEST INFRASTRUCTURE ONLY: the tests, the package smoke check and the bench's
 CPU-baseline leg use it; the HIP path never does.
@@ -20,6 +21,8 @@ HERE = Path(__file__).resolve().parent
 SOURCE = HERE / "attn_oracle.c"
 RMS_SOURCE = HERE / "rmsnorm_oracle.c"
 BWD_SOURCE = HERE / "attn_bwd_oracle.c"
+PAGED_SOURCE = HERE / "paged_oracle.c"
+SOURCES = (SOURCE, RMS_SOURCE, BWD_SOURCE, PAGED_SOURCE)
 LIBRARY = HERE / "liboracle_attn.so"
 
 DTYPE_F32 = 0
@@ -29,11 +32,11 @@ _c_double_p = ctypes.POINTER(ctypes.c_double)
 _c_int64_p = ctypes.POINTER(ctypes.c_int64)
 
 
-def build(source: Path = SOURCE, output: Path = LIBRARY, rms_source: Path = RMS_SOURCE,
-          bwd_source: Path = BWD_SOURCE) -> Path:
-    """Compile the oracle with gcc (plain -O2, OpenMP) into a shared library."""
+def build(sources=SOURCES, output: Path = LIBRARY) -> Path:
+    """Compile the oracle sources with gcc (plain -O2, OpenMP) into one shared
+    library."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-           str(source), str(rms_source), str(bwd_source), "-o", str(output) + ".tmp", "-lm"]
+           *[str(x) for x in sources], "-o", str(output) + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(str(output) + ".tmp", output)
     return output
@@ -65,6 +68,9 @@ class OracleLib:
         lib.tessera_oracle_attn_bwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
                                                 ctypes.c_double] + [_c_double_p] * 4
         lib.tessera_oracle_attn_bwd.restype = ctypes.c_int
+        lib.tessera_oracle_paged_decode.argtypes = [vp] * 5 + [ci] * 9 + [
+            ctypes.c_double, _c_double_p, _c_double_p]
+        lib.tessera_oracle_paged_decode.restype = ctypes.c_int
         lib.tessera_oracle_threads.argtypes = [ctypes.c_int]
         lib.tessera_oracle_threads.restype = ctypes.c_int
         self.lib = lib
@@ -185,6 +191,34 @@ class OracleLib:
         self._check(rc, "tessera_oracle_attn_bwd")
         return dq, dk, dv, delta
 
+    def paged_decode(self, q, k_cache, v_cache, block_table, context_lens, causal: bool,
+                     scale: float):
+        """Attention of the Tq newest query rows of each sequence over its K/V
+        held in a block-paged cache.  q [B,Hq,Tq,D] and the caches
+        [num_blocks,Hkv,block_size,D] are uint16 bf16 patterns; block_table
+        [B,max_blocks] and context_lens [B] are int32.  Returns O [B,Hq,Tq,D]
+        and lse [B,Hq,Tq], fp64 (rows that see no token: O = 0, lse = -inf)."""
+        q, kc, vc = (np.ascontiguousarray(a) for a in (q, k_cache, v_cache))
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        if q.dtype != np.uint16 or kc.dtype != np.uint16 or vc.dtype != np.uint16:
+            raise ValueError("paged_decode takes uint16 bf16 patterns")
+        if q.ndim != 4 or kc.ndim != 4 or kc.shape != vc.shape or bt.ndim != 2 or cl.ndim != 1:
+            raise ValueError("q [B,Hq,Tq,D], caches [num_blocks,Hkv,block_size,D], "
+                             "block_table [B,max_blocks], context_lens [B]")
+        B, Hq, Tq, D = q.shape
+        num_blocks, Hkv, block_size, Dk = kc.shape
+        if Dk != D or bt.shape[0] != B or cl.shape[0] != B:
+            raise ValueError("inconsistent paged-decode shapes")
+        O = np.empty((B, Hq, Tq, D), np.float64)
+        lse = np.empty((B, Hq, Tq), np.float64)
+        rc = self.lib.tessera_oracle_paged_decode(
+            self._ptr(q), self._ptr(kc), self._ptr(vc), self._ptr(bt), self._ptr(cl), B, Hq, Hkv,
+            Tq, D, block_size, bt.shape[1], num_blocks, int(bool(causal)), float(scale),
+            O.ctypes.data_as(_c_double_p), lse.ctypes.data_as(_c_double_p))
+        self._check(rc, "tessera_oracle_paged_decode")
+        return O, lse
+
     def threads(self, nthreads: int = 0) -> int:
         return int(self.lib.tessera_oracle_threads(int(nthreads)))
 
@@ -196,8 +230,7 @@ def load() -> OracleLib:
     """The oracle built from attn_oracle.c (compiled on first use if absent)."""
     global _DEFAULT
     if _DEFAULT is None:
-        newest = max(SOURCE.stat().st_mtime, RMS_SOURCE.stat().st_mtime,
-                     BWD_SOURCE.stat().st_mtime)
+        newest = max(src.stat().st_mtime for src in SOURCES)
         if not LIBRARY.exists() or LIBRARY.stat().st_mtime < newest:
             build()
         _DEFAULT = OracleLib(LIBRARY)
@@ -222,6 +255,10 @@ def attn_probs(q, k, v, causal, scale):
 
 def attn_bwd(q, k, v, dout, causal, scale):
     return load().attn_bwd(q, k, v, dout, causal, scale)
+
+
+def paged_decode(q, k_cache, v_cache, block_table, context_lens, causal, scale):
+    return load().paged_decode(q, k_cache, v_cache, block_table, context_lens, causal, scale)
 
 
 def rmsnorm(x, w, eps):

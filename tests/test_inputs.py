@@ -66,3 +66,32 @@ def test_kv_workload_counts_and_rows():
     qf, kf, vf = inputs.make_qkv(1, 2, 1, 9, 8, "bf16", 0)
     assert q.shape == (1, 2, 4, 8) and k.shape == (1, 1, 9, 8)
     assert torch.equal(q, qf[:, :, 5:]) and torch.equal(k, kf) and torch.equal(v, vf)
+
+
+def test_paged_inputs_structure():
+    """Every used block belongs to exactly one sequence, unused table entries
+    are -1, lengths are drawn in range, and the draw is seeded."""
+    q, kc, vc, table, lens = inputs.make_paged(6, 4, 2, 2, 32, 16, ctx_range=(1, 100), spare=5,
+                                               max_blocks=7, seed=4)
+    assert q.shape == (6, 4, 2, 32) and kc.shape == vc.shape and kc.shape[1:] == (2, 16, 32)
+    assert table.shape == (6, 7) and table.dtype == torch.int32 and lens.dtype == torch.int32
+    n = lens.numpy().astype(np.int64)
+    assert ((1 <= n) & (n <= 100)).all()
+    nblk = -(-n // 16)
+    used = np.concatenate([table[b, :nblk[b]].numpy() for b in range(6)])
+    assert len(set(used.tolist())) == used.size == nblk.sum()
+    assert kc.shape[0] == used.size + 5 and (used >= 0).all() and (used < kc.shape[0]).all()
+    assert all((table[b, nblk[b]:] == -1).all() for b in range(6))
+    again = inputs.make_paged(6, 4, 2, 2, 32, 16, ctx_range=(1, 100), spare=5, max_blocks=7,
+                              seed=4)
+    assert all(torch.equal(a, b) for a, b in zip((q, kc, vc, table, lens), again))
+
+
+def test_paged_workload_and_bytes():
+    w = inputs.PAGED_WORKLOADS["decode_b64_ctx16k_d128"]
+    assert (w.B, w.Hq, w.Hkv, w.Tq, w.D, w.block_size) == (64, 32, 8, 1, 128, 16)
+    assert w.max_blocks == 1024
+    # one sequence of 17 tokens, Hkv = 2, D = 8, blocks of 16: K and V rows,
+    # q and out (bf16), lse (fp32), two table entries and one length
+    got = inputs.paged_bytes([17], Hq=4, Hkv=2, Tq=1, D=8, block_size=16)
+    assert got == 2 * 2 * 2 * 8 * 17 + 2 * 2 * 4 * 8 + 4 * 4 + 4 * 2 + 4

@@ -9,10 +9,11 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.oracle import BWD_SOURCE, RMS_SOURCE, SOURCE, OracleLib
+from oracle.oracle import BWD_SOURCE, PAGED_SOURCE, RMS_SOURCE, SOURCE, OracleLib
 from tests import oracle_pins
 from tests.oracle_pins import ALL_PINS, rand_inputs
 from tests.attn_bwd_pins import ALL_BWD_PINS
+from tests.paged_pins import ALL_PAGED_PINS
 from tests.rmsnorm_pins import ALL_RMS_PINS
 
 
@@ -21,7 +22,8 @@ def lib():
     return oracle.load()
 
 
-@pytest.mark.parametrize("pin", ALL_PINS + ALL_RMS_PINS + ALL_BWD_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", ALL_PINS + ALL_RMS_PINS + ALL_BWD_PINS + ALL_PAGED_PINS,
+                         ids=lambda f: f.__name__)
 def test_pin(lib, pin):
     pin(lib)
 
@@ -84,15 +86,54 @@ BWD_MUTANTS = {
 }
 
 
-def build_mutant(tmp_path: Path, attn_src: str, rms_src: str, bwd_src: str = None) -> OracleLib:
-    a, r, w = tmp_path / "mutant_attn.c", tmp_path / "mutant_rms.c", tmp_path / "mutant_bwd.c"
-    a.write_text(attn_src)
-    r.write_text(rms_src)
-    w.write_text(bwd_src if bwd_src is not None else BWD_SOURCE.read_text())
+# The same for the paged-decode oracle.  Every mutant still reads only the
+# blocks the table names for the sequence (a wrong block index could read past
+# the cache and crash the test process instead of failing a pin).
+PAGED_MUTANTS = {
+    "interleaved_head_map": ("const int g = h / G;", "const int g = h % Hkv;"),
+    "row_shifted_in_block": ("* block_size + t % block_size) * D;",
+                             "* block_size + (t + 1) % block_size) * D;"),
+    "mask_hides_newest": ("int vis = causal ? n - Tq + i + 1 : n;",
+                          "int vis = causal ? n - Tq + i : n;"),
+    "mask_ignored": ("int vis = causal ? n - Tq + i + 1 : n;", "int vis = n;"),
+    "mask_from_front": ("int vis = causal ? n - Tq + i + 1 : n;",
+                        "int vis = causal ? i + 1 : n;"),
+    "scale_dropped": ("s[t] = scale * dot;", "s[t] = dot;"),
+    "values_from_keys": ("o[d] += w * widen16(v_cache, row + d);",
+                         "o[d] += w * widen16(k_cache, row + d);"),
+    "lse_without_max": ("= m + log(Z);", "= log(Z);"),
+    "empty_row_lse_zero": ("lse[((int64_t)b * Hq + h) * Tq + i] = -INFINITY;",
+                           "lse[((int64_t)b * Hq + h) * Tq + i] = 0.0;"),
+    "unnormalised": ("const double w = s[t] / Z;", "const double w = s[t];"),
+    "query_from_head_zero": ("const int64_t qi = (((int64_t)b * Hq + h) * Tq + i) * D;",
+                             "const int64_t qi = (((int64_t)b * Hq + 0 * h) * Tq + i) * D;"),
+}
+
+
+def build_mutant(tmp_path: Path, attn_src: str = None, rms_src: str = None, bwd_src: str = None,
+                 paged_src: str = None) -> OracleLib:
+    """The oracle library built from the given sources (the real file for each
+    one not given)."""
+    texts = [(attn_src, SOURCE), (rms_src, RMS_SOURCE), (bwd_src, BWD_SOURCE),
+             (paged_src, PAGED_SOURCE)]
+    files = []
+    for i, (text, real) in enumerate(texts):
+        f = tmp_path / f"mutant_{i}.c"
+        f.write_text(text if text is not None else real.read_text())
+        files.append(str(f))
     so = tmp_path / "libmutant.so"
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", str(a), str(r),
-                    str(w), "-o", str(so), "-lm"], check=True)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", *files, "-o",
+                    str(so), "-lm"], check=True)
     return OracleLib(so)
+
+
+@pytest.mark.parametrize("name", sorted(PAGED_MUTANTS))
+def test_planted_paged_mistake_is_caught(tmp_path: Path, name):
+    old, new = PAGED_MUTANTS[name]
+    src = PAGED_SOURCE.read_text()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutant = build_mutant(tmp_path, paged_src=src.replace(old, new, 1))
+    assert caught_by(mutant, ALL_PAGED_PINS), f"no pin rejects the planted mistake {name}"
 
 
 @pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
@@ -100,8 +141,7 @@ def test_planted_backward_mistake_is_caught(tmp_path: Path, name):
     old, new = BWD_MUTANTS[name]
     src = BWD_SOURCE.read_text()
     assert src.count(old) >= 1, f"mutation anchor for {name} not found"
-    mutant = build_mutant(tmp_path, SOURCE.read_text(), RMS_SOURCE.read_text(),
-                          src.replace(old, new, 1))
+    mutant = build_mutant(tmp_path, bwd_src=src.replace(old, new, 1))
     assert caught_by(mutant, ALL_BWD_PINS), f"no pin rejects the planted mistake {name}"
 
 
@@ -120,7 +160,7 @@ def test_planted_rmsnorm_mistake_is_caught(tmp_path: Path, name):
     old, new = RMS_MUTANTS[name]
     src = RMS_SOURCE.read_text()
     assert src.count(old) >= 1, f"mutation anchor for {name} not found"
-    mutant = build_mutant(tmp_path, SOURCE.read_text(), src.replace(old, new, 1))
+    mutant = build_mutant(tmp_path, rms_src=src.replace(old, new, 1))
     assert caught_by(mutant, ALL_RMS_PINS), f"no pin rejects the planted mistake {name}"
 
 
@@ -129,7 +169,7 @@ def test_planted_mistake_is_caught(tmp_path: Path, name):
     old, new = MUTANTS[name]
     src = SOURCE.read_text()
     assert src.count(old) >= 1, f"mutation anchor for {name} not found"
-    mutant = build_mutant(tmp_path, src.replace(old, new, 1), RMS_SOURCE.read_text())
+    mutant = build_mutant(tmp_path, attn_src=src.replace(old, new, 1))
     caught = []
     for pin in ALL_PINS:
         try:
@@ -173,3 +213,19 @@ def test_pins_module_is_standalone():
     # the pins must not lean on the HIP package
     text = Path(oracle_pins.__file__).read_text()
     assert "attention_flashattention_fwd_amd" not in text
+
+
+def test_paged_argument_errors(lib):
+    from tests.paged_pins import rand_paged
+    q, kc, vc, table, lens = rand_paged(2, 4, 2, 1, 8, 16, [5, 20], seed=3)
+    lib.paged_decode(q, kc, vc, table, lens, True, 0.5)
+    too_long = lens.copy()
+    too_long[1] = table.shape[1] * 16 + 1
+    with pytest.raises(RuntimeError):
+        lib.paged_decode(q, kc, vc, table, too_long, True, 0.5)
+    bad = table.copy()
+    bad[1, 1] = kc.shape[0]
+    with pytest.raises(RuntimeError):
+        lib.paged_decode(q, kc, vc, bad, lens, True, 0.5)
+    with pytest.raises(ValueError):
+        lib.paged_decode(q, kc, vc[:, :1], table, lens, True, 0.5)
