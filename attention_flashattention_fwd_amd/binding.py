@@ -1,4 +1,5 @@
-"""Thin ctypes binding over the C ABI in include/tessera_attn.h.
+"""Thin ctypes binding over the C ABI in include/*.h (tessera_attn.h,
+tessera_attn_bwd.h, tessera_paged.h, tessera_rmsnorm.h).
 
 Argument marshalling only: every step of the attention forward pass runs in
 the HIP kernels of libtessera_attn.so.  torch supplies device memory and the
@@ -28,10 +29,11 @@ ERR_ALIAS = 7
 ERR_TOO_LARGE = 8
 ERR_LAUNCH = 9
 ERR_EPS = 10
+ERR_WORKSPACE = 11
 
 EXPORTS = ("tessera_attn_fwd", "tessera_attn_fwd_kv", "tessera_attn_fwd_f32", "tessera_attn_bwd",
            "tessera_attn_status_string", "tessera_attn_last_error", "tessera_attn_version",
-           "tessera_rmsnorm_fwd")
+           "tessera_rmsnorm_fwd", "tessera_paged_decode", "tessera_paged_decode_workspace")
 
 _lib = None
 
@@ -61,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.tessera_attn_bwd.restype = i
         L.tessera_rmsnorm_fwd.argtypes = [vp, vp, vp, ctypes.c_longlong, i, f, vp]
         L.tessera_rmsnorm_fwd.restype = i
+        L.tessera_paged_decode.argtypes = [vp] * 7 + [i] * 9 + [f, vp, ctypes.c_longlong, vp]
+        L.tessera_paged_decode.restype = i
+        L.tessera_paged_decode_workspace.argtypes = [i] * 7
+        L.tessera_paged_decode_workspace.restype = ctypes.c_longlong
         L.tessera_attn_status_string.argtypes = [i]
         L.tessera_attn_status_string.restype = ctypes.c_char_p
         L.tessera_attn_last_error.argtypes = []
@@ -294,3 +300,102 @@ def attn_bwd(q, k, v, out, lse, dout, causal: bool = True, scale: float | None =
             msg += ": " + lib().tessera_attn_last_error().decode()
         raise RuntimeError(f"tessera_attn_bwd failed ({st}): {msg}")
     return dq, dk, dv, delta
+
+
+def raw_paged_workspace(B, Hq, Hkv, Tq, D, block_size, max_blocks) -> int:
+    """tessera_paged_decode_workspace: bytes needed, or -status."""
+    return int(lib().tessera_paged_decode_workspace(int(B), int(Hq), int(Hkv), int(Tq), int(D),
+                                                    int(block_size), int(max_blocks)))
+
+
+def raw_paged(q, kc, vc, table, lens, out, lse, B, Hq, Hkv, Tq, D, num_blocks, block_size,
+              max_blocks, causal, scale, ws, ws_bytes, stream) -> int:
+    """Call tessera_paged_decode with integer device addresses; returns the status."""
+    return int(lib().tessera_paged_decode(q, kc, vc, table, lens, out, lse, int(B), int(Hq),
+                                          int(Hkv), int(Tq), int(D), int(num_blocks),
+                                          int(block_size), int(max_blocks), int(causal),
+                                          float(np.float32(scale)), ws, int(ws_bytes), stream))
+
+
+def _check_paged(q, k_cache, v_cache, block_table, context_lens):
+    import torch
+
+    for name, t, dt, nd in (("q", q, torch.bfloat16, 4), ("k_cache", k_cache, torch.bfloat16, 4),
+                            ("v_cache", v_cache, torch.bfloat16, 4),
+                            ("block_table", block_table, torch.int32, 2),
+                            ("context_lens", context_lens, torch.int32, 1)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a torch.Tensor on a GPU device")
+        if t.dtype != dt or t.dim() != nd or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {nd}-D {dt} tensor")
+        if t.device != q.device:
+            raise ValueError("all paged-decode tensors must be on one device")
+    B, Hq, Tq, D = q.shape
+    num_blocks, Hkv, block_size, Dk = k_cache.shape
+    if v_cache.shape != k_cache.shape or Dk != D or block_table.shape[0] != B \
+            or context_lens.shape != (B,):
+        raise ValueError("q [B,Hq,Tq,D], caches [num_blocks,Hkv,block_size,D], "
+                         "block_table [B,max_blocks], context_lens [B]")
+    return B, Hq, Hkv, Tq, D, num_blocks, block_size, block_table.shape[1]
+
+
+def paged_workspace_bytes(B, Hq, Hkv, Tq, D, block_size, max_blocks) -> int:
+    """Bytes of workspace tessera_paged_decode needs (raises on bad sizes)."""
+    n = raw_paged_workspace(B, Hq, Hkv, Tq, D, block_size, max_blocks)
+    if n < 0:
+        raise RuntimeError(f"tessera_paged_decode_workspace failed ({-n}): {status_string(-n)}")
+    return n
+
+
+def paged_decode_into(q, k_cache, v_cache, block_table, context_lens, out, lse, workspace,
+                      causal: bool = True, scale: float | None = None, stream=None) -> None:
+    """Decode attention over a block-paged cache into preallocated out
+    [B,Hq,Tq,D] bfloat16 and lse [B,Hq,Tq] float32; `workspace` is a uint8
+    tensor of at least paged_workspace_bytes(...) bytes (or None when that is 0)."""
+    import torch
+
+    B, Hq, Hkv, Tq, D, nblk, bs, maxb = _check_paged(q, k_cache, v_cache, block_table,
+                                                      context_lens)
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32 or lse.device != q.device \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Tq] on q's device")
+    ws, ws_bytes = 0, 0
+    if workspace is not None:
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        ws, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = raw_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                       block_table.data_ptr(), context_lens.data_ptr(), out.data_ptr(),
+                       lse.data_ptr(), B, Hq, Hkv, Tq, D, nblk, bs, maxb, int(bool(causal)),
+                       scale, ws, ws_bytes, handle)
+    if st != OK:
+        msg = status_string(st)
+        if st == ERR_LAUNCH:
+            msg += ": " + lib().tessera_attn_last_error().decode()
+        raise RuntimeError(f"tessera_paged_decode failed ({st}): {msg}")
+
+
+def paged_decode(q, k_cache, v_cache, block_table, context_lens, causal: bool = True,
+                 scale: float | None = None):
+    """Attention of the Tq newest tokens of each sequence over its K/V in a
+    block-paged cache (layout in include/tessera_paged.h).  Returns
+    (out [B,Hq,Tq,D] bfloat16, lse [B,Hq,Tq] float32)."""
+    import torch
+
+    B, Hq, Hkv, Tq, D, _, bs, maxb = _check_paged(q, k_cache, v_cache, block_table,
+                                                   context_lens)
+    n = paged_workspace_bytes(B, Hq, Hkv, Tq, D, bs, maxb)
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    paged_decode_into(q, k_cache, v_cache, block_table, context_lens, out, lse, ws, causal, scale)
+    return out, lse

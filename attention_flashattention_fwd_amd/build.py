@@ -1,5 +1,5 @@
 """Build the gfx950 HIP library in-tree: libtessera_attn.so beside this file
-(the attention forward and backward, and the fused RMSNorm).
+(the attention forward and backward, paged decode, and the fused RMSNorm).
 
     python -m attention_flashattention_fwd_amd.build
 """
@@ -14,7 +14,7 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 SOURCES = [PKG / "csrc" / "tessera_attn.hip", PKG / "csrc" / "tessera_attn_bwd.hip",
-           PKG / "csrc" / "tessera_rmsnorm.hip"]
+           PKG / "csrc" / "tessera_rmsnorm.hip", PKG / "csrc" / "tessera_paged.hip"]
 INCLUDE = ROOT / "include"
 LIBRARY = PKG / "libtessera_attn.so"
 ARCH = "gfx950"

@@ -21,7 +21,7 @@
 
 #include "tessera_attn.h"
 
-#define TESSERA_VERSION 10100
+#define TESSERA_VERSION 10200
 
 namespace {
 
@@ -893,7 +893,9 @@ extern "C" const char *tessera_attn_status_string(int status) {
     case TESSERA_ERR_SHAPE:
         return "bad shape: B, Hq, Hkv and the row counts must be >= 1, Hq % Hkv == 0, and a "
                "causal call needs no more query rows than key rows";
-    case TESSERA_ERR_UNSUPPORTED: return "unsupported head dim: D must be 32, 64 or 128";
+    case TESSERA_ERR_UNSUPPORTED:
+        return "unsupported size: D must be 32, 64 or 128 (RMSNorm: n a multiple of 8, at most "
+               "65536; paged decode: (Hq / Hkv) * Tq <= 32, block_size a multiple of 16)";
     case TESSERA_ERR_CAUSAL: return "causal must be 0 or 1";
     case TESSERA_ERR_SCALE: return "scale must be finite";
     case TESSERA_ERR_ALIGN: return "misaligned pointer: q, k, v, out need 16 bytes, lse 4 bytes";
@@ -901,6 +903,7 @@ extern "C" const char *tessera_attn_status_string(int status) {
     case TESSERA_ERR_TOO_LARGE: return "problem too large for one launch grid";
     case TESSERA_ERR_LAUNCH: return "HIP kernel launch failed";
     case TESSERA_ERR_EPS: return "eps must be finite and non-negative";
+    case TESSERA_ERR_WORKSPACE: return "workspace missing or smaller than required";
     default: return "unknown status";
     }
 }

@@ -55,6 +55,8 @@ def parse_args(argv=None):
                    help="only time the attention backward workload(s) (profiling runs)")
     p.add_argument("--rmsnorm-only", action="store_true",
                    help="only time the fused RMSNorm workload(s) (profiling runs)")
+    p.add_argument("--paged-only", action="store_true",
+                   help="only time the paged-decode workload(s) (profiling runs)")
     p.add_argument("--hbm-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (to scale HBM counters)")
     p.add_argument("--gemm-calibration", action="store_true",
@@ -291,6 +293,58 @@ def main(argv=None):
         print(json.dumps(backward_lines()))
         return 0
 
+    def paged_lines():
+        """Decode over the block-paged cache (HBM-bound): the bytes one call must
+        move (every cached K/V row once, q, out, lse, table entries) over the
+        time of the call (split kernel plus merge kernel).  Four sequences of the
+        timed output, the longest among them, are checked against the oracle."""
+        import numpy as np
+
+        import oracle
+
+        res = {}
+        for name, pw in inputs.PAGED_WORKLOADS.items():
+            q, kc, vc, table, cl = inputs.make_paged_workload(pw)
+            qd, kd, vd, td, cd = (t.to(dev) for t in (q, kc, vc, table, cl))
+            out = torch.empty_like(qd)
+            lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+            nws = binding.paged_workspace_bytes(pw.B, pw.Hq, pw.Hkv, pw.Tq, pw.D, pw.block_size,
+                                                pw.max_blocks)
+            ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
+            torch.cuda.synchronize()
+            fn = lambda: binding.paged_decode_into(qd, kd, vd, td, cd, out, lse, ws,  # noqa: E731
+                                                   pw.causal, pw.scale, stream=stream)
+            p_ms, _, p_med, p_min = time_steps(torch, fn, max(20, args.steps), args.warmup,
+                                               stream, warm_seconds=0.2)
+            nbytes = inputs.paged_bytes(cl.numpy(), pw.Hq, pw.Hkv, pw.Tq, pw.D, pw.block_size)
+            gbs = nbytes / (p_ms * 1e-3) / 1e9
+            n = cl.numpy()
+            pick = np.array(sorted({int(n.argmax()), 0, pw.B // 2, pw.B - 1}))
+            O_ref, l_ref = oracle.paged_decode(inputs.bits(q[pick]), inputs.bits(kc),
+                                               inputs.bits(vc), table.numpy()[pick], n[pick],
+                                               pw.causal, pw.scale)
+            o = out[torch.from_numpy(pick).to(dev)].float().cpu().numpy()
+            lg = lse[torch.from_numpy(pick).to(dev)].cpu().numpy()
+            eo, el = float(np.abs(o - O_ref).max()), float(np.abs(lg - l_ref).max())
+            res[name] = {
+                "config": pw.describe(),
+                "tokens_cached": int(n.sum()),
+                "bytes_per_call": nbytes,
+                "us_per_call": round(p_ms * 1e3, 2),
+                "us_median": round(p_med * 1e3, 2),
+                "us_min": round(p_min * 1e3, 2),
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                             "kernel": f"paged_decode_kernel<{pw.D}> + paged_combine_kernel"},
+                "parity": {"sequences": pick.tolist(), "max_abs_err_O": eo,
+                           "max_abs_err_lse": el, "ok": eo <= 2e-2 and el <= 2e-2},
+            }
+        return res
+
+    if args.paged_only:
+        print(json.dumps(paged_lines()))
+        return 0
+
     def measure(name, steps, warmup, with_cpu, warm_seconds=0.0):
         if name in inputs.KV_WORKLOADS:   # Tq new rows against Tk cached rows
             w = inputs.KV_WORKLOADS[name]
@@ -344,6 +398,7 @@ def main(argv=None):
 
     secondary.update(rmsnorm_lines() if not args.no_secondary else {})
     secondary.update(backward_lines() if not args.no_secondary else {})
+    secondary.update(paged_lines() if not args.no_secondary else {})
 
     line = {
         "metric": "attention fwd TFLOP/s (causal-adjusted) and % of MI355X bf16 MFMA peak",

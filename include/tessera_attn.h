@@ -48,14 +48,16 @@ enum tessera_attn_status {
     TESSERA_ERR_NULL = 1,        /* a pointer argument is NULL */
     TESSERA_ERR_SHAPE = 2,       /* B, Hq, Hkv or a row count < 1, Hq % Hkv != 0, or a
                                     causal tessera_attn_fwd_kv call with Tq > Tk */
-    TESSERA_ERR_UNSUPPORTED = 3, /* D is not 32, 64 or 128 */
+    TESSERA_ERR_UNSUPPORTED = 3, /* D is not 32, 64 or 128, or another size limit of the
+                                    called function is exceeded */
     TESSERA_ERR_CAUSAL = 4,      /* causal is neither 0 nor 1 */
     TESSERA_ERR_SCALE = 5,       /* scale is NaN or infinite */
     TESSERA_ERR_ALIGN = 6,       /* q, k, v, out not 16-byte or lse not 4-byte aligned */
     TESSERA_ERR_ALIAS = 7,       /* out or lse overlaps an input or each other */
     TESSERA_ERR_TOO_LARGE = 8,   /* the launch grid would exceed 2^31 - 1 workgroups */
     TESSERA_ERR_LAUNCH = 9,      /* the HIP kernel launch failed */
-    TESSERA_ERR_EPS = 10         /* RMSNorm eps is NaN, infinite or negative */
+    TESSERA_ERR_EPS = 10,        /* RMSNorm eps is NaN, infinite or negative */
+    TESSERA_ERR_WORKSPACE = 11   /* paged decode workspace NULL or too small */
 };
 
 /*

@@ -18,7 +18,7 @@ Q, K, V, O, L = (1 << 44), (2 << 44), (3 << 44), (4 << 44), (5 << 44)
 def declared_functions():
     names = set()
     for h in HEADERS:
-        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tessera_\w+)\s*\(",
+        names |= set(re.findall(r"^\s*(?:const\s+)?(?:\w+\s+)*?\w+\s*\*?\s*(tessera_\w+)\s*\(",
                                 h.read_text(), re.M))
     return sorted(names)
 
@@ -31,11 +31,11 @@ def test_library_loads_and_exports_every_symbol():
     lib = binding.lib()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert binding.version() == 10100
+    assert binding.version() == 10200
 
 
 def test_status_strings():
-    for code in range(0, 11):
+    for code in range(0, 12):
         assert binding.status_string(code)
     assert binding.status_string(123) == "unknown status"
     assert binding.lib().tessera_attn_last_error() == b""
@@ -149,3 +149,55 @@ def call_bwd(q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, dl=DL, B=1, Hq
 ])
 def test_bwd_bad_arguments_are_rejected_before_launch(kwargs, code):
     assert call_bwd(**kwargs) == code
+
+
+def test_paged_workspace_sizes():
+    # the serving batch: 64 x 8 (sequence, KV head) pairs of up to 16384 tokens
+    # -> splits of 512 keys, 32 per sequence; 2048 query rows
+    cells = 64 * 32 * 1 * 32
+    assert binding.raw_paged_workspace(64, 32, 8, 1, 128, 16, 1024) == cells * 4 + cells * 128 * 4
+    # short sequences fit one split: no workspace
+    assert binding.raw_paged_workspace(2, 4, 2, 1, 64, 16, 8) == 0
+    # 1600 tokens in splits of 256: 7 per sequence; the lse part rounds up to 256 bytes
+    cells = 1 * 8 * 2 * 7
+    assert binding.raw_paged_workspace(1, 8, 2, 2, 32, 16, 100) == 512 + cells * 32 * 4
+    assert binding.raw_paged_workspace(1, 8, 2, 9, 32, 16, 100) == -binding.ERR_UNSUPPORTED
+    assert binding.raw_paged_workspace(1, 8, 2, 1, 32, 24, 100) == -binding.ERR_UNSUPPORTED
+    assert binding.raw_paged_workspace(1, 8, 3, 1, 32, 16, 100) == -binding.ERR_SHAPE
+    assert binding.raw_paged_workspace(1, 8, 2, 1, 32, 16, 1 << 28) == -binding.ERR_TOO_LARGE
+
+
+KC, VC, BT, CL, WS = (14 << 44), (15 << 44), (16 << 44), (17 << 44), (18 << 44)
+
+
+def call_paged(q=Q, kc=KC, vc=VC, bt=BT, cl=CL, o=O, l=L, B=2, Hq=8, Hkv=2, Tq=2, D=64,
+               num_blocks=64, block_size=16, max_blocks=100, causal=1, scale=0.125, ws=WS,
+               ws_bytes=1 << 20):
+    return binding.raw_paged(q, kc, vc, bt, cl, o, l, B, Hq, Hkv, Tq, D, num_blocks, block_size,
+                             max_blocks, causal, scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(bt=None), binding.ERR_NULL),
+    (dict(cl=None), binding.ERR_NULL),
+    (dict(num_blocks=0), binding.ERR_SHAPE),
+    (dict(max_blocks=0), binding.ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), binding.ERR_SHAPE),
+    (dict(D=96), binding.ERR_UNSUPPORTED),
+    (dict(Tq=9), binding.ERR_UNSUPPORTED),           # 4 heads x 9 rows > 32
+    (dict(block_size=8), binding.ERR_UNSUPPORTED),
+    (dict(causal=2), binding.ERR_CAUSAL),
+    (dict(scale=float("nan")), binding.ERR_SCALE),
+    (dict(kc=KC + 8), binding.ERR_ALIGN),
+    (dict(ws=WS + 4), binding.ERR_ALIGN),
+    (dict(cl=CL + 2), binding.ERR_ALIGN),
+    (dict(max_blocks=1 << 28), binding.ERR_TOO_LARGE),
+    (dict(ws=None), binding.ERR_WORKSPACE),
+    (dict(ws_bytes=100), binding.ERR_WORKSPACE),
+    (dict(o=KC + 4096), binding.ERR_ALIAS),         # out inside the K cache
+    (dict(l=BT), binding.ERR_ALIAS),
+    (dict(ws=CL), binding.ERR_ALIAS),
+    (dict(ws=O + 1024), binding.ERR_ALIAS),          # workspace over out
+])
+def test_paged_bad_arguments_are_rejected_before_launch(kwargs, code):
+    assert call_paged(**kwargs) == code
