@@ -56,7 +56,7 @@ constexpr int kTileKeys = 32;          // keys per LDS stage
 constexpr int kMaxCols = 32;           // query rows per (sequence, KV head)
 constexpr int kMaxEntries = 64;        // table entries of one split: one per lane
 constexpr int kMinSplit = 256;         // keys per split, at least (before rounding)
-constexpr int64_t kTargetUnits = 16384;   // (sequence, KV head, split) units aimed for
+constexpr int64_t kTargetUnits = 8192;    // (sequence, KV head, split) units aimed for
 constexpr uint32_t kBadBits = 0x7fc00000u;    // quiet NaN: marks bad table data
 constexpr uint16_t kBadBf16 = 0x7fc0u;
 
@@ -106,6 +106,16 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// A wave-uniform pointer in scalar registers.  The base of every load below
+// is uniform by construction; this states it for the compiler, whose
+// divergence analysis does not always see it.
+__device__ __forceinline__ const char *uniform_ptr(const char *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // One 16-byte global->LDS load per lane (base + voff -> lds + 16 * lane),
 // untracked by the compiler: the kernel waits for it with an explicit vmcnt.
 // The s_nop covers the M0-write hazard before the load.
@@ -114,7 +124,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(voff), "s"(base), "s"(lds)
+                 : "v"(voff), "s"(uniform_ptr((const char *)base)), "s"(lds)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop

@@ -153,8 +153,9 @@ def test_bwd_bad_arguments_are_rejected_before_launch(kwargs, code):
 
 def test_paged_workspace_sizes():
     # the serving batch: 64 x 8 (sequence, KV head) pairs of up to 16384 tokens
-    # -> splits of 512 keys, 32 per sequence; 2048 query rows
-    cells = 64 * 32 * 1 * 32
+    # -> splits of 1024 keys (64 blocks of 16, the most one split may span),
+    # 16 per sequence; 2048 query rows
+    cells = 64 * 32 * 1 * 16
     assert binding.raw_paged_workspace(64, 32, 8, 1, 128, 16, 1024) == cells * 4 + cells * 128 * 4
     # short sequences fit one split: no workspace
     assert binding.raw_paged_workspace(2, 4, 2, 1, 64, 16, 8) == 0
