@@ -65,6 +65,14 @@ def parse_args(argv=None):
     return p.parse_args(argv)
 
 
+_T0 = time.perf_counter()
+
+
+def progress(msg: str) -> None:
+    """One line on stderr per finished phase (the JSON line stays alone on stdout)."""
+    print(f"bench: {msg} ({time.perf_counter() - _T0:.0f} s)", file=sys.stderr, flush=True)
+
+
 def source_digest() -> str:
     """SHA-256 prefix of the kernel source with comments and whitespace runs
     removed: a comment edit keeps the recorded counters valid, a code edit
@@ -249,6 +257,7 @@ def main(argv=None):
             c_ms, _, _, _ = time_steps(torch, lambda: yd.copy_(xd), max(20, args.steps),
                                        args.warmup, stream, warm_seconds=0.1)
             copy_gbs = 2.0 * xd.numel() * 2 / (c_ms * 1e-3) / 1e9
+            progress(f"rmsnorm {name} timed")
             res[name] = {
                 "config": rw.describe(),
                 "us_per_call": round(r_ms * 1e3, 2),
@@ -280,6 +289,7 @@ def main(argv=None):
             b_ms, _, b_med, _ = time_steps(torch, fn, max(5, args.steps // 5), args.warmup,
                                            stream, warm_seconds=0.2)
             tf = 2.5 * w.flops / (b_ms * 1e-3) / 1e12
+            progress(f"backward {name} timed")
             res[f"bwd_{name}"] = {
                 "config": w.describe() + ", backward (dq, dk, dv)",
                 "us_per_call": round(b_ms * 1e3, 2),
@@ -326,6 +336,7 @@ def main(argv=None):
             o = out[torch.from_numpy(pick).to(dev)].float().cpu().numpy()
             lg = lse[torch.from_numpy(pick).to(dev)].cpu().numpy()
             eo, el = float(np.abs(o - O_ref).max()), float(np.abs(lg - l_ref).max())
+            progress(f"paged decode {name} timed and checked")
             res[name] = {
                 "config": pw.describe(),
                 "tokens_cached": int(n.sum()),
@@ -366,8 +377,10 @@ def main(argv=None):
         gpu_ms, wall_ms, med_ms, min_ms = time_steps(torch, fn, steps, warmup, stream,
                                                      warm_seconds)
         res = {"w": w, "gpu_ms": gpu_ms, "wall_ms": wall_ms, "med_ms": med_ms, "min_ms": min_ms}
+        progress(f"forward {name} timed")
         if with_cpu:
             res["cpu"], res["parity"] = cpu_baseline(w, q, k, v, out, lse, args.cpu_seconds)
+            progress("cpu baseline and parity sample done")
         return res
 
     if args.workload not in inputs.WORKLOADS and args.workload not in inputs.KV_WORKLOADS:
