@@ -209,7 +209,7 @@ def test_binding_argument_checks():
         binding.attn_fwd(q.transpose(1, 2), k, k)
     with pytest.raises(RuntimeError, match="shape"):
         binding.attn_fwd(torch.zeros(1, 3, 16, 64, dtype=torch.bfloat16, device="cuda"), k, k)
-    with pytest.raises(RuntimeError, match="head dim"):
+    with pytest.raises(RuntimeError, match="D must be 32, 64 or 128"):
         binding.attn_fwd(q[..., :48].contiguous(), k[..., :48].contiguous(),
                          k[..., :48].contiguous())
 
