@@ -171,6 +171,16 @@ __device__ __forceinline__ void pack_steps(u32x4 (&out)[4], const f32x16 &a, con
     }
 }
 
+// Packs one f32x16 MFMA result (32 rows) into the bf16 B-operand words of its
+// two 16-row steps.
+__device__ __forceinline__ void pack_half(u32x4 (&out)[2], const f32x16 &a) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bf16x2 p = __builtin_convertvector((f32x2){a[2 * e], a[2 * e + 1]}, bf16x2);
+        out[e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p);
+    }
+}
+
 // Writes a [D, 32] accumulator (lane: column col of its 32, dims of every
 // block) times `mul` as bf16 row `row` of a [rows, D] tensor.
 template <int D>
@@ -205,11 +215,12 @@ struct BwdArgs {
 // ---------------------------------------------------------------------------
 // dq (and Delta): a workgroup of NW waves per query tile of 32 * nqb rows and
 // hg query heads of one KV head; wave w takes head w % hg and query block
-// w / hg, as in the forward.  D = 128 needs more than 256 registers per
-// wave, so it runs 4 waves (one per SIMD, up to 512 each); smaller D run 8.
+// w / hg, as in the forward.  Eight waves, two per SIMD (at most 256
+// registers each, which D = 128 fits by taking a tile's keys in two halves),
+// so that one wave's matrix-core work hides the other's latencies.
 // ---------------------------------------------------------------------------
 template <int D>
-constexpr int kDqWaves = D == 128 ? 4 : 8;
+constexpr int kDqWaves = 8;
 
 template <int D, int NW = kDqWaves<D>>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
@@ -281,45 +292,40 @@ attn_bwd_dq_kernel(BwdArgs a) {
         }
         const LDS_AS char *kt = (const LDS_AS char *)lds_k[cur];
         const LDS_AS char *vt = (const LDS_AS char *)lds_v[cur];
-        f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            s0 = mfma32(read_row<D>(kt, off, 0, ks), qf[ks], s0);
-            s1 = mfma32(read_row<D>(kt, off, 1, ks), qf[ks], s1);
-            p0 = mfma32(read_row<D>(vt, off, 0, ks), dof[ks], p0);
-            p1 = mfma32(read_row<D>(vt, off, 1, ks), dof[ks], p1);
-        }
-        // exponent of P; keys hidden from this query (causal) or past T get -inf
         const int j0 = t * kTileRows;
-        f32x16 x0, x1;
+        const bool masked = j0 + kTileRows > T || (causal && j0 + kTileRows - 1 > qw0);
+        // The tile's keys in two 32-key halves (S, dP, dS and the dq update of
+        // one half at a time), which keeps the registers of a wave within 256.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            x0[i] = __builtin_fmaf(s0[i], c, -lse2);
-            x1[i] = __builtin_fmaf(s1[i], c, -lse2);
-        }
-        if (j0 + kTileRows > T || (causal && j0 + kTileRows - 1 > qw0)) {
-            const int last = (causal ? qrow : T - 1) - j0 - 4 * hi;
+        for (int h = 0; h < 2; ++h) {
+            f32x16 sh = {}, ph = {};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 8 * (i >> 2) + (i & 3);
-                if (r > last) x0[i] = -INFINITY;
-                if (r + 32 > last) x1[i] = -INFINITY;
+            for (int ks = 0; ks < D / 16; ++ks) {
+                sh = mfma32(read_row<D>(kt, off, h, ks), qf[ks], sh);
+                ph = mfma32(read_row<D>(vt, off, h, ks), dof[ks], ph);
             }
-        }
-        f32x16 d0, d1;   // dS
+            // exponent of P; keys hidden from this query (causal) or past T get -inf
+            f32x16 x;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            d0[i] = __builtin_amdgcn_exp2f(x0[i]) * (p0[i] - dl);
-            d1[i] = __builtin_amdgcn_exp2f(x1[i]) * (p1[i] - dl);
-        }
-        u32x4 dsu[4];
-        pack_steps(dsu, d0, d1);
+            for (int i = 0; i < 16; ++i) x[i] = __builtin_fmaf(sh[i], c, -lse2);
+            if (masked) {
+                const int last = (causal ? qrow : T - 1) - j0 - 32 * h - 4 * hi;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+                for (int i = 0; i < 16; ++i)
+                    if (8 * (i >> 2) + (i & 3) > last) x[i] = -INFINITY;
+            }
+            f32x16 d;   // dS
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-                acc[db] = mfma32(read_tr<D>(kt, off, st, db), __builtin_bit_cast(bf16x8, dsu[st]),
-                                 acc[db]);
+            for (int i = 0; i < 16; ++i) d[i] = __builtin_amdgcn_exp2f(x[i]) * (ph[i] - dl);
+            u32x4 dsu[2];
+            pack_half(dsu, d);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    acc[db] = mfma32(read_tr<D>(kt, off, 2 * h + st, db),
+                                     __builtin_bit_cast(bf16x8, dsu[st]), acc[db]);
+            }
         }
         if (t + 1 < ntiles) {
             ks_.store((LDS_AS char *)lds_k[cur ^ 1], tid);
