@@ -337,17 +337,23 @@ attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv: a workgroup of 4 waves (one per SIMD, up to 512 registers each) per
-// 128-key tile of one KV head; wave w owns keys k0 + 32 w .. +31.  It loops
-// over the query heads of the group and, for each, over the 64-row query
-// tiles that can see these keys.
+// dk, dv: a workgroup of 8 waves per 128-key tile of one KV head, two per
+// SIMD (at most 256 registers each).  Waves w and w + 4 own keys
+// k0 + 32 (w % 4) .. +31: wave w (w < 4) forms S and P and accumulates
+// dv^T += dO^T P, wave w + 4 forms S, dP and dS and accumulates
+// dk^T += Q^T dS.  Each holds half the accumulators a wave doing both would
+// need (S is formed twice), and the two waves of a SIMD overlap one's matrix
+// work with the other's vector work.  The workgroup loops over the query
+// heads of the group and, for each, over the 64-row query tiles that can see
+// these keys, whose Q and dO rows stream through LDS shared by all eight
+// waves; each tile is taken in two 32-row halves.
 // ---------------------------------------------------------------------------
-constexpr int kKvWaves = 4;
+constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
-constexpr int kKeyTile = 32 * kKvWaves;
+constexpr int kKeyTile = 128;
 
 template <int D>
-__global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds_q[2][Tile<D>::kBytes];
     __shared__ __attribute__((aligned(16))) char lds_d[2][Tile<D>::kBytes];
@@ -356,6 +362,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool dk_wave = w >= 4;   // wave-uniform role
     const int hi = lane >> 5, col = lane & 31;
 
     // key tile 0 first: under the causal mask it has the most query rows after it
@@ -366,21 +373,18 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     const int T = a.T;
     const bool causal = a.causal != 0;
     const int k0 = kt_idx * kKeyTile;
-    const int kw0 = k0 + 32 * w;
+    const int kw0 = k0 + 32 * (w & 3);
     const int key = kw0 + col;
 
     const uint16_t *khead = a.k + (int64_t)bh * T * D;
     const uint16_t *vhead = a.v + (int64_t)bh * T * D;
     bf16x8 kf[D / 16], vf[D / 16];
     load_fragment<D>(kf, khead, kw0, T, lane);
-    load_fragment<D>(vf, vhead, kw0, T, lane);
+    if (dk_wave) load_fragment<D>(vf, vhead, kw0, T, lane);
 
-    f32x16 adk[D / 32], adv[D / 32];
+    f32x16 acc[D / 32];   // dv^T or dk^T of this wave's keys
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        adk[db] = f32x16{};
-        adv[db] = f32x16{};
-    }
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
     const TileOffsets<D> off(lane);
     const float c = a.c;
 
@@ -423,59 +427,51 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
         const int q0 = (qt_first + step % per_head) * kTileRows;
         const LDS_AS char *qt = (const LDS_AS char *)lds_q[cur];
         const LDS_AS char *dt = (const LDS_AS char *)lds_d[cur];
-        f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            s0 = mfma32(read_row<D>(qt, off, 0, ks), kf[ks], s0);
-            s1 = mfma32(read_row<D>(qt, off, 1, ks), kf[ks], s1);
-            p0 = mfma32(read_row<D>(dt, off, 0, ks), vf[ks], p0);
-            p1 = mfma32(read_row<D>(dt, off, 1, ks), vf[ks], p1);
-        }
-        // Lane: key column `key`; register i of block bl holds query row
-        // q0 + 32 bl + 8 (i / 4) + 4 hi + i % 4.
         const bool need_mask = causal && q0 < kw0 + 31;
-        f32x16 e0, e1, d0, d1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 8 * j + 4 * hi;
-            const f32x4 la = *(const LDS_AS f32x4 *)&lds_l[cur][r];
-            const f32x4 lb = *(const LDS_AS f32x4 *)&lds_l[cur][r + 32];
-            const f32x4 ma = *(const LDS_AS f32x4 *)&lds_m[cur][r];
-            const f32x4 mb = *(const LDS_AS f32x4 *)&lds_m[cur][r + 32];
+        for (int h = 0; h < 2; ++h) {
+            // Lane: key column `key`; register i holds query row
+            // q0 + 32 h + 8 (i / 4) + 4 hi + i % 4.
+            f32x16 sh = {}, ph = {};
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = 4 * j + u;
-                float xa = __builtin_fmaf(s0[i], c, -la[u]);
-                float xb = __builtin_fmaf(s1[i], c, -lb[u]);
-                if (need_mask) {
-                    if (q0 + r + u < key) xa = -INFINITY;
-                    if (q0 + 32 + r + u < key) xb = -INFINITY;
-                }
-                e0[i] = __builtin_amdgcn_exp2f(xa);
-                e1[i] = __builtin_amdgcn_exp2f(xb);
-                d0[i] = e0[i] * (p0[i] - ma[u]);
-                d1[i] = e1[i] * (p1[i] - mb[u]);
+            for (int ks = 0; ks < D / 16; ++ks) sh = mfma32(read_row<D>(qt, off, h, ks), kf[ks], sh);
+            if (dk_wave) {
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks)
+                    ph = mfma32(read_row<D>(dt, off, h, ks), vf[ks], ph);
             }
-        }
-        u32x4 pu[4], dsu[4];
-        pack_steps(pu, e0, e1);
-        pack_steps(dsu, d0, d1);
+            f32x16 x;   // P, then dS on the dk waves
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+            for (int j = 0; j < 4; ++j) {
+                const int r = 32 * h + 8 * j + 4 * hi;
+                const f32x4 l4 = *(const LDS_AS f32x4 *)&lds_l[cur][r];
+                const f32x4 m4 = *(const LDS_AS f32x4 *)&lds_m[cur][r];
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                adv[db] = mfma32(read_tr<D>(dt, off, st, db), __builtin_bit_cast(bf16x8, pu[st]),
-                                 adv[db]);
-                adk[db] = mfma32(read_tr<D>(qt, off, st, db), __builtin_bit_cast(bf16x8, dsu[st]),
-                                 adk[db]);
+                for (int u = 0; u < 4; ++u) {
+                    const int i = 4 * j + u;
+                    float xe = __builtin_fmaf(sh[i], c, -l4[u]);
+                    if (need_mask && q0 + r + u < key) xe = -INFINITY;
+                    const float e = __builtin_amdgcn_exp2f(xe);
+                    x[i] = dk_wave ? e * (ph[i] - m4[u]) : e;
+                }
+            }
+            u32x4 xu[2];
+            pack_half(xu, x);
+            const LDS_AS char *src = dk_wave ? qt : dt;   // Q^T for dk, dO^T for dv
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    acc[db] = mfma32(read_tr<D>(src, off, 2 * h + st, db),
+                                     __builtin_bit_cast(bf16x8, xu[st]), acc[db]);
             }
         }
         if (step + 1 < nsteps) store(cur ^ 1);
         __syncthreads();
     }
     if (key < T) {
-        store_rows<D>(a.dk + ((int64_t)bh * T + key) * D, adk, a.scale, hi);
-        store_rows<D>(a.dv + ((int64_t)bh * T + key) * D, adv, 1.f, hi);
+        if (dk_wave) store_rows<D>(a.dk + ((int64_t)bh * T + key) * D, acc, a.scale, hi);
+        else store_rows<D>(a.dv + ((int64_t)bh * T + key) * D, acc, 1.f, hi);
     }
 }
 
