@@ -159,6 +159,17 @@ __device__ __forceinline__ void load_fragment(bf16x8 (&f)[D / 16], const uint16_
     for (int ks = 0; ks < D / 16; ++ks) f[ks] = *(const bf16x8 *)(src + 16 * ks);
 }
 
+// Workgroup barrier that publishes this wave's LDS writes but, unlike
+// __syncthreads(), does not wait for its global loads in flight (the next
+// tile's rows).  The empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Packs two f32x16 MFMA results (rows 0-31 and 32-63 of a 64-row step
 // sequence) into the four bf16 B-operand words per 16-row step.
 __device__ __forceinline__ void pack_steps(u32x4 (&out)[4], const f32x16 &a, const f32x16 &b) {
@@ -340,13 +351,13 @@ attn_bwd_dq_kernel(BwdArgs a) {
 // dk, dv: a workgroup of 8 waves per 128-key tile of one KV head, two per
 // SIMD (at most 256 registers each).  Waves w and w + 4 own keys
 // k0 + 32 (w % 4) .. +31: wave w (w < 4) forms S and P and accumulates
-// dv^T += dO^T P, wave w + 4 forms S, dP and dS and accumulates
-// dk^T += Q^T dS.  Each holds half the accumulators a wave doing both would
-// need (S is formed twice), and the two waves of a SIMD overlap one's matrix
-// work with the other's vector work.  The workgroup loops over the query
-// heads of the group and, for each, over the 64-row query tiles that can see
-// these keys, whose Q and dO rows stream through LDS shared by all eight
-// waves; each tile is taken in two 32-row halves.
+// dv^T += dO^T P; wave w + 4 forms dP, takes P from wave w through LDS,
+// forms dS and accumulates dk^T += Q^T dS.  Each holds one set of
+// accumulators and executes half the products, and the two waves of a SIMD
+// overlap one's matrix work with the other's vector work.  The workgroup
+// loops over the query heads of the group and, for each, over the 64-row
+// query tiles that can see these keys, whose Q and dO rows stream through
+// LDS shared by all eight waves; each tile is taken in two 32-row halves.
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
@@ -359,6 +370,9 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds_d[2][Tile<D>::kBytes];
     __shared__ __attribute__((aligned(16))) float lds_l[2][kTileRows];   // lse * log2 e
     __shared__ __attribute__((aligned(16))) float lds_m[2][kTileRows];   // Delta
+    // P of one 32-row half from each dv wave to its dk wave: [half][pair][k][lane]
+    // holds the lane's P registers 4k .. 4k+3.
+    __shared__ __attribute__((aligned(16))) f32x4 lds_p[2][4][4][64];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -378,9 +392,8 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 
     const uint16_t *khead = a.k + (int64_t)bh * T * D;
     const uint16_t *vhead = a.v + (int64_t)bh * T * D;
-    bf16x8 kf[D / 16], vf[D / 16];
-    load_fragment<D>(kf, khead, kw0, T, lane);
-    if (dk_wave) load_fragment<D>(vf, vhead, kw0, T, lane);
+    bf16x8 kv[D / 16];   // K (S on the dv waves) or V (dP on the dk waves)
+    load_fragment<D>(kv, dk_wave ? vhead : khead, kw0, T, lane);
 
     f32x16 acc[D / 32];   // dv^T or dk^T of this wave's keys
 #pragma unroll
@@ -431,32 +444,43 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             // Lane: key column `key`; register i holds query row
-            // q0 + 32 h + 8 (i / 4) + 4 hi + i % 4.
-            f32x16 sh = {}, ph = {};
+            // q0 + 32 h + 8 (i / 4) + 4 hi + i % 4.  The dv wave forms S
+            // (from Q) and P, the dk wave dP (from dO).
+            f32x16 sp = {};
+            const LDS_AS char *lhs = dk_wave ? dt : qt;
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) sh = mfma32(read_row<D>(qt, off, h, ks), kf[ks], sh);
-            if (dk_wave) {
+            for (int ks = 0; ks < D / 16; ++ks) sp = mfma32(read_row<D>(lhs, off, h, ks), kv[ks], sp);
+            f32x4 (&xp)[4][64] = lds_p[h][w & 3];
+            if (!dk_wave) {
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks)
-                    ph = mfma32(read_row<D>(dt, off, h, ks), vf[ks], ph);
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 32 * h + 8 * j + 4 * hi;
+                    const f32x4 l4 = *(const LDS_AS f32x4 *)&lds_l[cur][r];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int i = 4 * j + u;
+                        float xe = __builtin_fmaf(sp[i], c, -l4[u]);
+                        if (need_mask && q0 + r + u < key) xe = -INFINITY;
+                        sp[i] = __builtin_amdgcn_exp2f(xe);
+                    }
+                    *(LDS_AS f32x4 *)&xp[j][lane] =
+                        f32x4{sp[4 * j], sp[4 * j + 1], sp[4 * j + 2], sp[4 * j + 3]};
+                }
             }
-            f32x16 x;   // P, then dS on the dk waves
+            lds_barrier();   // P is in LDS
+            if (dk_wave) {
+                // dS = P (dP - Delta)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 32 * h + 8 * j + 4 * hi;
-                const f32x4 l4 = *(const LDS_AS f32x4 *)&lds_l[cur][r];
-                const f32x4 m4 = *(const LDS_AS f32x4 *)&lds_m[cur][r];
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 32 * h + 8 * j + 4 * hi;
+                    const f32x4 m4 = *(const LDS_AS f32x4 *)&lds_m[cur][r];
+                    const f32x4 p4 = *(const LDS_AS f32x4 *)&xp[j][lane];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int i = 4 * j + u;
-                    float xe = __builtin_fmaf(sh[i], c, -l4[u]);
-                    if (need_mask && q0 + r + u < key) xe = -INFINITY;
-                    const float e = __builtin_amdgcn_exp2f(xe);
-                    x[i] = dk_wave ? e * (ph[i] - m4[u]) : e;
+                    for (int u = 0; u < 4; ++u) sp[4 * j + u] = p4[u] * (sp[4 * j + u] - m4[u]);
                 }
             }
             u32x4 xu[2];
-            pack_half(xu, x);
+            pack_half(xu, sp);
             const LDS_AS char *src = dk_wave ? qt : dt;   // Q^T for dk, dO^T for dv
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
