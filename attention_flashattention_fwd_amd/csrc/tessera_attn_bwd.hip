@@ -349,7 +349,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dk, dv: a workgroup of 8 waves per 128-key tile of one KV head, two per
-// SIMD (at most 256 registers each).  Waves w and w + 4 own keys
+// SIMD (at most 256 registers each; at D <= 64 two workgroups share a CU).  Waves w and w + 4 own keys
 // k0 + 32 (w % 4) .. +31: wave w (w < 4) forms S and P and accumulates
 // dv^T += dO^T P; wave w + 4 forms dP, takes P from wave w through LDS,
 // forms dS and accumulates dk^T += Q^T dS.  Each holds one set of
@@ -362,9 +362,15 @@ attn_bwd_dq_kernel(BwdArgs a) {
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKeyTile = 128;
+// Waves per SIMD the dk/dv kernel is built for: at D <= 64 a wave fits 128
+// registers and the workgroup's LDS (66 KB at D = 64) leaves room for a second
+// workgroup per CU, whose waves hide the first's barrier and load waits.
+template <int D>
+constexpr int kKvWavesPerSimd = D == 128 ? 2 : 4;
 
 template <int D>
-__global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kKvThreads)
+__attribute__((amdgpu_waves_per_eu(kKvWavesPerSimd<D>, kKvWavesPerSimd<D>)))
 attn_bwd_dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds_q[2][Tile<D>::kBytes];
     __shared__ __attribute__((aligned(16))) char lds_d[2][Tile<D>::kBytes];
