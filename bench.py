@@ -138,6 +138,16 @@ def time_steps(torch, fn, steps, warmup, stream, warm_seconds=0.0):
     return gpu_ms, wall * 1e3 / steps, per[len(per) // 2], per[0]
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(w, q, k, v, out, lse, budget_s):
     """The fp64 oracle on random query rows of the workload until the time
     budget is spent; rate in TFLOP/s with the same causal-adjusted flop count
@@ -181,18 +191,10 @@ def cpu_baseline(w, q, k, v, out, lse, budget_s):
         "ok": bool(eo.max() <= 2e-2 and eo.mean() <= 2e-3 and el.max() <= 2e-2
                    and el.mean() <= 2e-3),
     }
-    cpu_model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu_model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
     baseline = {
         "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": (f"{len(rows)} random query rows of the same workload ({flops / 1e9:.1f} "
-                   f"GFLOP, {elapsed:.1f} s, fp64, OpenMP {threads} threads, {cpu_model})"),
+                   f"GFLOP, {elapsed:.1f} s, fp64, OpenMP {threads} threads, {cpu_model()})"),
     }
     return baseline, parity
 
@@ -257,7 +259,21 @@ def main(argv=None):
             c_ms, _, _, _ = time_steps(torch, lambda: yd.copy_(xd), max(20, args.steps),
                                        args.warmup, stream, warm_seconds=0.1)
             copy_gbs = 2.0 * xd.numel() * 2 / (c_ms * 1e-3) / 1e9
-            progress(f"rmsnorm {name} timed")
+            fn()   # the copy above overwrote y
+            torch.cuda.synchronize()
+            # the oracle on a sample of rows (CPU baseline), which also checks them
+            import numpy as np
+
+            import oracle
+            rows = np.arange(rw.rows)   # every row: the oracle takes milliseconds here
+            xb, wb = inputs.bits(x), inputs.bits(g)
+            t0 = time.perf_counter()
+            y_ref = oracle.rmsnorm(xb[rows], wb, rw.eps)
+            cpu_s = time.perf_counter() - t0
+            y = yd[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64)
+            bound = (2.0 ** -8 + (rw.n / 64 + 16) * 2.0 ** -24) * np.abs(y_ref)
+            worst = float(np.max(np.abs(y - y_ref) / np.maximum(bound, 1e-300)))
+            progress(f"rmsnorm {name} timed and checked")
             res[name] = {
                 "config": rw.describe(),
                 "us_per_call": round(r_ms * 1e3, 2),
@@ -265,6 +281,13 @@ def main(argv=None):
                 "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                              "device_copy_gbs": round(copy_gbs, 1)},
+                "cpu_baseline": {
+                    "value": round(2.0 * (2 * len(rows) * rw.n + rw.n) / cpu_s / 1e9, 3),
+                    "unit": "GB/s", "cores": oracle.threads(0), "kind": "oracle",
+                    "sample": (f"all {len(rows)} rows of the same workload ({cpu_s:.3f} s, "
+                               f"fp64, {cpu_model()})")},
+                "parity": {"rows": len(rows), "worst_error_over_bound": worst,
+                           "ok": worst <= 1.0},
             }
         return res
 
@@ -290,13 +313,53 @@ def main(argv=None):
                                            stream, warm_seconds=0.2)
             tf = 2.5 * w.flops / (b_ms * 1e-3) / 1e12
             progress(f"backward {name} timed")
-            res[f"bwd_{name}"] = {
+            # The oracle on the first KV head group of batch element 0 (its G
+            # query heads, all T rows), which also checks that slice of the
+            # timed output against the derived bar (max-abs 2^-6 of max |X|,
+            # mean-abs 2^-7 of RMS(X)).  Only where that slice is small: the
+            # fp64 oracle runs at a few GFLOP/s.
+            import numpy as np
+
+            import oracle
+            G = w.Hq // w.Hkv
+            slice_flops = 2.5 * w.flops * G / (w.B * w.Hq)
+            line = {
                 "config": w.describe() + ", backward (dq, dk, dv)",
                 "us_per_call": round(b_ms * 1e3, 2),
                 "us_median": round(b_med * 1e3, 2),
                 "tflops": round(tf, 1),
                 "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
             }
+            res[f"bwd_{name}"] = line
+            if slice_flops > 5e10:
+                line["cpu_baseline"] = None
+                line["parity"] = {"note": "oracle slice too large for the default run "
+                                          f"({slice_flops / 1e9:.0f} GFLOP)"}
+                continue
+            dq, dk, dv, _ = fn()
+            torch.cuda.synchronize()
+            sl = [inputs.bits(t[:1, :G]) for t in (q, do)]
+            kv1 = [inputs.bits(t[:1, :1]) for t in (k, v)]
+            t0 = time.perf_counter()
+            rq, rk, rv, _ = oracle.attn_bwd(sl[0], kv1[0], kv1[1], sl[1], w.causal, w.scale)
+            cpu_s = time.perf_counter() - t0
+            worst = 0.0
+            for got, ref in ((dq[:1, :G], rq), (dk[:1, :1], rk), (dv[:1, :1], rv)):
+                e = np.abs(got.float().cpu().numpy().astype(np.float64) - ref)
+                scale_max, scale_rms = np.abs(ref).max(), np.sqrt(np.mean(ref * ref))
+                worst = max(worst, e.max() / (2.0 ** -6 * scale_max),
+                            e.mean() / (2.0 ** -7 * scale_rms))
+            progress(f"backward {name} oracle slice done")
+            line.update({
+                "cpu_baseline": {
+                    "value": round(slice_flops / cpu_s / 1e12, 5), "unit": "TFLOP/s",
+                    "cores": oracle.threads(0), "kind": "oracle",
+                    "sample": (f"batch element 0, query heads 0..{G - 1} with KV head 0, all "
+                               f"{w.T} rows ({slice_flops / 1e9:.1f} GFLOP counted as 2.5x the "
+                               f"forward's, {cpu_s:.1f} s, fp64, {cpu_model()})")},
+                "parity": {"slice": "b=0, KV head 0", "worst_error_over_bar": float(worst),
+                           "ok": bool(worst <= 1.0)},
+            })
         return res
 
     if args.backward_only:
@@ -330,9 +393,12 @@ def main(argv=None):
             gbs = nbytes / (p_ms * 1e-3) / 1e9
             n = cl.numpy()
             pick = np.array(sorted({int(n.argmax()), 0, pw.B // 2, pw.B - 1}))
+            t0 = time.perf_counter()
             O_ref, l_ref = oracle.paged_decode(inputs.bits(q[pick]), inputs.bits(kc),
                                                inputs.bits(vc), table.numpy()[pick], n[pick],
                                                pw.causal, pw.scale)
+            cpu_s = time.perf_counter() - t0
+            cpu_bytes = inputs.paged_bytes(n[pick], pw.Hq, pw.Hkv, pw.Tq, pw.D, pw.block_size)
             o = out[torch.from_numpy(pick).to(dev)].float().cpu().numpy()
             lg = lse[torch.from_numpy(pick).to(dev)].cpu().numpy()
             eo, el = float(np.abs(o - O_ref).max()), float(np.abs(lg - l_ref).max())
@@ -347,6 +413,12 @@ def main(argv=None):
                 "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                              "kernel": f"paged_decode_kernel<{pw.D}> + paged_combine_kernel"},
+                "cpu_baseline": {
+                    "value": round(cpu_bytes / cpu_s / 1e9, 3), "unit": "GB/s",
+                    "cores": oracle.threads(0), "kind": "oracle",
+                    "sample": (f"sequences {pick.tolist()} of the same batch "
+                               f"({int(n[pick].sum())} cached tokens, {cpu_s:.2f} s, fp64, "
+                               f"{cpu_model()})")},
                 "parity": {"sequences": pick.tolist(), "max_abs_err_O": eo,
                            "max_abs_err_lse": el, "ok": eo <= 2e-2 and el <= 2e-2},
             }

@@ -3,12 +3,16 @@ against the fp64 oracle.
 
 The GPU forward supplies out and lse (as a training step would); the oracle
 computes the exact gradients from q, k, v and dout alone.  Bar, per tensor X
-of the reference (dq, dk, dv, Delta): max-abs error <= 2^-7 max|X| and
-mean-abs error <= 2^-7 RMS(X), one bf16 ulp of the tensor's own scale.  The
+of the reference (dq, dk, dv, Delta): max-abs error <= 2^-6 max|X| and
+mean-abs error <= 2^-7 RMS(X).  The pages fix no precision for gradients; the
 pipeline rounds P and dS to bf16 for the matrix cores, takes Delta from the
-bf16 forward output, and rounds each result to bf16; the oracle's arithmetic
-with just those roundings added (a CPU check) already lands at 0.2-0.5 % of
-max|X| and 0.2-0.3 % of RMS(X), the size of what the GPU shows.
+bf16 forward output, and rounds each result to bf16.  The oracle's arithmetic
+with just those roundings added (a CPU emulation) lands at 0.2-0.5 % of
+max|X| on N(0,1) inputs, and at 1.01 * 2^-7 max|dk| on the T=4096 workload
+whose Q and K carry x8 outlier entries (dk sums many bf16-rounded dS terms
+with large q entries); the GPU matches the emulation there.  The max-abs bar
+is therefore two bf16 ulps of max|X|, the mean-abs bar one ulp of RMS(X)
+(emulation and GPU at most 0.19 of it).
 """
 from __future__ import annotations
 
@@ -23,6 +27,10 @@ from attention_flashattention_fwd_amd import binding, inputs
 from tests.test_gpu_parity import say
 
 pytestmark = pytest.mark.gpu
+
+
+MAX_BAR = 2.0 ** -6    # of max|X|
+MEAN_BAR = 2.0 ** -7   # of RMS(X)
 
 
 def make_bwd(B, Hq, Hkv, T, D, seed):
@@ -51,8 +59,8 @@ def run_case(B, Hq, Hkv, T, D, causal, seed, scale=None):
         e = np.abs(g - ref)
         stats.append(f"{name} max {e.max():.2e} ({e.max() / max(top, 1e-30):.2%} of max) "
                      f"mean {e.mean():.2e} ({e.mean() / max(rms, 1e-30):.2%} of rms)")
-        assert e.max() <= 2.0 ** -7 * top and e.mean() <= 2.0 ** -7 * rms, (name, e.max(),
-                                                                              e.mean(), top, rms)
+        assert e.max() <= MAX_BAR * top and e.mean() <= MEAN_BAR * rms, (name, e.max(),
+                                                                            e.mean(), top, rms)
     say(" | ".join(stats))
 
 
@@ -86,3 +94,34 @@ def test_bwd_repeatable():
     b = binding.attn_bwd(q, k, v, out, lse, do)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_bwd_outlier_workload_slice():
+    """The T=4096 workload with x8 outlier entries in Q and K (B=16 Hq=16 Hkv=4
+    D=64), in the bench's launch: the whole batch on the GPU, the gradients of
+    batch element 0, KV head 0 and its four query heads checked against the
+    oracle (the bench's dout: torch.randn, seed 7)."""
+    w = inputs.WORKLOADS["t4096_outliers"]
+    q, k, v = inputs.make_workload(w)
+    g = torch.Generator().manual_seed(7)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    say(f"case bwd workload {w.name}: {w.describe()}, slice b=0 KV head 0")
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    out, lse = binding.attn_fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    dq, dk, dv, delta = binding.attn_bwd(qd, kd, vd, out, lse, dod, causal=w.causal,
+                                         scale=w.scale)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    r = oracle.attn_bwd(inputs.bits(q[:1, :G]), inputs.bits(k[:1, :1]), inputs.bits(v[:1, :1]),
+                        inputs.bits(do[:1, :G]), w.causal, w.scale)
+    stats = []
+    for name, got, ref in zip(("dq", "dk", "dv", "delta"),
+                              (dq[:1, :G], dk[:1, :1], dv[:1, :1], delta[:1, :G]), r):
+        gv = got.float().cpu().numpy().astype(np.float64)
+        top, rms = float(np.abs(ref).max()), float(np.sqrt((ref ** 2).mean()))
+        e = np.abs(gv - ref)
+        stats.append(f"{name} max {e.max() / (MAX_BAR * top):.3f} of bar, "
+                     f"mean {e.mean() / (MEAN_BAR * rms):.3f} of bar")
+        assert e.max() <= MAX_BAR * top and e.mean() <= MEAN_BAR * rms, (name, e.max(), e.mean())
+    say(" | ".join(stats))
