@@ -349,8 +349,9 @@ attn_bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dk, dv: a workgroup of 8 waves per 128-key tile of one KV head, two per
-// SIMD (at most 256 registers each; at D <= 64 two workgroups share a CU).  Waves w and w + 4 own keys
-// k0 + 32 (w % 4) .. +31: wave w (w < 4) forms S and P and accumulates
+// SIMD (at most 256 registers each; at D <= 64 two workgroups share a CU).
+// Waves w and w + 4 own keys k0 + 32 (w % 4) .. +31: wave w (w < 4) forms S
+// and P and accumulates
 // dv^T += dO^T P; wave w + 4 forms dP, takes P from wave w through LDS,
 // forms dS and accumulates dk^T += Q^T dS.  Each holds one set of
 // accumulators and executes half the products, and the two waves of a SIMD
@@ -505,6 +506,183 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
+// dk, dv at D = 128, with the hand-over of P one step late.  The roles are
+// those of attn_bwd_dkdv_kernel, but the dk wave forms dS and dk for step
+// s - 1 while the dv wave works on step s, so the P it reads was published
+// by the barrier that ends every step and no barrier is needed inside one
+// (at D = 128 one workgroup fills a CU, and nothing else hides those).  Q
+// tiles, lse and Delta therefore stay in LDS one step longer (three
+// buffers), P is double-buffered by step, and the loop runs one step past
+// the last tile for the dk wave.  Same arithmetic, in the same order.
+template <int D>
+__global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dkdv_lag_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds_q[3][Tile<D>::kBytes];
+    __shared__ __attribute__((aligned(16))) char lds_d[2][Tile<D>::kBytes];
+    __shared__ __attribute__((aligned(16))) float lds_l[3][kTileRows];   // lse * log2 e
+    __shared__ __attribute__((aligned(16))) float lds_m[3][kTileRows];   // Delta
+    // P of step s in [s % 2][half][pair][k][lane] (the lane's P registers 4k .. 4k+3)
+    __shared__ __attribute__((aligned(16))) f32x4 lds_p[2][2][4][4][64];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool dk_wave = w >= 4;   // wave-uniform role
+    const int hi = lane >> 5, col = lane & 31;
+
+    const int kt_idx = (int)(blockIdx.x / a.nbh);
+    const int bh = blockIdx.x - kt_idx * a.nbh;
+    const int b = bh / a.Hkv;
+    const int hkv = bh - b * a.Hkv;
+    const int T = a.T;
+    const bool causal = a.causal != 0;
+    const int k0 = kt_idx * kKeyTile;
+    const int kw0 = k0 + 32 * (w & 3);
+    const int key = kw0 + col;
+
+    const uint16_t *khead = a.k + (int64_t)bh * T * D;
+    const uint16_t *vhead = a.v + (int64_t)bh * T * D;
+    bf16x8 kv[D / 16];   // K (S on the dv waves) or V (dP on the dk waves)
+    load_fragment<D>(kv, dk_wave ? vhead : khead, kw0, T, lane);
+
+    f32x16 acc[D / 32];   // dv^T or dk^T of this wave's keys
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    const TileOffsets<D> off(lane);
+    const float c = a.c;
+
+    const int qt_first = causal ? k0 / kTileRows : 0;
+    const int nq = (T + kTileRows - 1) / kTileRows;
+    const int per_head = nq - qt_first;
+    const int nsteps = a.G * per_head;
+    const int64_t head0 = (int64_t)b * a.Hq + (int64_t)hkv * a.G;
+
+    TileStager<D, kKvThreads> qs_, ds_;
+    float l_in = 0.f, m_in = 0.f;
+    auto fetch = [&](int step) __attribute__((always_inline)) {
+        const int g = step / per_head, q0 = (qt_first + step % per_head) * kTileRows;
+        const int64_t hrow = (head0 + g) * T;
+        qs_.fetch(a.q + hrow * D, q0, T, tid);
+        ds_.fetch(a.dout + hrow * D, q0, T, tid);
+        if (tid < kTileRows) {
+            const bool ok = q0 + tid < T;
+            l_in = ok ? a.lse[hrow + q0 + tid] * kLog2e : INFINITY;   // P = 0 past T
+            m_in = ok ? a.delta[hrow + q0 + tid] : 0.f;
+        }
+    };
+    auto store = [&](int step) __attribute__((always_inline)) {
+        const int b3 = step % 3;
+        qs_.store((LDS_AS char *)lds_q[b3], tid);
+        ds_.store((LDS_AS char *)lds_d[step & 1], tid);
+        if (tid < kTileRows) {
+            lds_l[b3][tid] = l_in;
+            lds_m[b3][tid] = m_in;
+        }
+    };
+    auto q0_of = [&](int step) { return (qt_first + step % per_head) * kTileRows; };
+
+    fetch(0);
+    store(0);
+    __syncthreads();
+    // Each role runs its own loop (registers are allocated per role); both
+    // pass the same barriers, one per step, and share the tile staging.
+    auto step_end = [&](int step) __attribute__((always_inline)) {
+        if (step + 1 < nsteps) store(step + 1);
+        __syncthreads();
+    };
+    if (!dk_wave) {
+        for (int step = 0; step <= nsteps; ++step) {
+            if (step + 1 < nsteps) fetch(step + 1);
+            if (step < nsteps) {
+                const int q0 = q0_of(step);
+                const bool need_mask = causal && q0 < kw0 + 31;
+                const LDS_AS char *qt = (const LDS_AS char *)lds_q[step % 3];
+                const LDS_AS char *dt = (const LDS_AS char *)lds_d[step & 1];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    // register i holds query row q0 + 32 h + 8 (i / 4) + 4 hi + i % 4
+                    f32x16 sp = {};
+#pragma unroll
+                    for (int ks = 0; ks < D / 16; ++ks)
+                        sp = mfma32(read_row<D>(qt, off, h, ks), kv[ks], sp);
+                    f32x4 (&xp)[4][64] = lds_p[step & 1][h][w & 3];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 32 * h + 8 * j + 4 * hi;
+                        const f32x4 l4 = *(const LDS_AS f32x4 *)&lds_l[step % 3][r];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int i = 4 * j + u;
+                            float xe = __builtin_fmaf(sp[i], c, -l4[u]);
+                            if (need_mask && q0 + r + u < key) xe = -INFINITY;
+                            sp[i] = __builtin_amdgcn_exp2f(xe);
+                        }
+                        *(LDS_AS f32x4 *)&xp[j][lane] =
+                            f32x4{sp[4 * j], sp[4 * j + 1], sp[4 * j + 2], sp[4 * j + 3]};
+                    }
+                    u32x4 xu[2];
+                    pack_half(xu, sp);
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                        for (int db = 0; db < D / 32; ++db)
+                            acc[db] = mfma32(read_tr<D>(dt, off, 2 * h + st, db),
+                                             __builtin_bit_cast(bf16x8, xu[st]), acc[db]);
+                    }
+                }
+            }
+            step_end(step);
+        }
+    } else {
+        f32x16 dp[2];   // dP of the step before (both halves)
+        for (int step = 0; step <= nsteps; ++step) {
+            if (step + 1 < nsteps) fetch(step + 1);
+            if (step > 0) {
+                // dS and dk of the step before: its Q tile, Delta and P are still in LDS
+                const int prev = step - 1;
+                const LDS_AS char *qt = (const LDS_AS char *)lds_q[prev % 3];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f32x4 (&xp)[4][64] = lds_p[prev & 1][h][w & 3];
+                    f32x16 ds;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 32 * h + 8 * j + 4 * hi;
+                        const f32x4 m4 = *(const LDS_AS f32x4 *)&lds_m[prev % 3][r];
+                        const f32x4 p4 = *(const LDS_AS f32x4 *)&xp[j][lane];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            ds[4 * j + u] = p4[u] * (dp[h][4 * j + u] - m4[u]);
+                    }
+                    u32x4 xu[2];
+                    pack_half(xu, ds);
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                        for (int db = 0; db < D / 32; ++db)
+                            acc[db] = mfma32(read_tr<D>(qt, off, 2 * h + st, db),
+                                             __builtin_bit_cast(bf16x8, xu[st]), acc[db]);
+                    }
+                }
+            }
+            if (step < nsteps) {
+                const LDS_AS char *dt = (const LDS_AS char *)lds_d[step & 1];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    dp[h] = f32x16{};
+#pragma unroll
+                    for (int ks = 0; ks < D / 16; ++ks)
+                        dp[h] = mfma32(read_row<D>(dt, off, h, ks), kv[ks], dp[h]);
+                }
+            }
+            step_end(step);
+        }
+    }
+    if (key < T) {
+        if (dk_wave) store_rows<D>(a.dk + ((int64_t)bh * T + key) * D, acc, a.scale, hi);
+        else store_rows<D>(a.dv + ((int64_t)bh * T + key) * D, acc, 1.f, hi);
+    }
+}
+
 bool overlaps(const void *x, size_t nx, const void *y, size_t ny) {
     const uintptr_t p = (uintptr_t)x, q = (uintptr_t)y;
     return p < q + ny && q < p + nx;
@@ -573,7 +751,7 @@ extern "C" int tessera_attn_bwd(const void *q, const void *k, const void *v, con
     // dq first: it writes the Delta rows the dk/dv kernel reads.
     if (D == 128) {
         hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, g1, b1, 0, s, a);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, g2, b2, 0, s, a);
+        hipLaunchKernelGGL(attn_bwd_dkdv_lag_kernel<128>, g2, b2, 0, s, a);
     } else if (D == 64) {
         hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, g1, b1, 0, s, a);
         hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, g2, b2, 0, s, a);
