@@ -16,18 +16,20 @@
 //     streams K and V tiles, forms S^T = K Q^T and dP^T = V dO^T on the
 //     matrix cores, P and dS on the vector ALUs, and dq^T += K^T dS^T.  It
 //     also writes Delta, from the dO and O rows it holds.
-//   * attn_bwd_dkdv_kernel: a workgroup per 128-key tile of one KV head; it
-//     streams the Q and dO tiles of every query head of the group, forms
-//     S = Q K^T and dP = dO V^T, and accumulates dv^T += dO^T P and
+//   * attn_bwd_dkdv_kernel (attn_bwd_dkdv_lag_kernel at D = 128): a
+//     workgroup per 128-key tile of one KV head; it streams the Q and dO
+//     tiles of every query head of the group.  Two roles per key block: one
+//     wave forms S = Q K^T and P and accumulates dv^T += dO^T P, the other
+//     forms dP = dO V^T, takes P from the first through LDS and accumulates
 //     dk^T += Q^T dS.
-// Both use v_mfma_f32_32x32x16_bf16 in the transposed form of the forward:
+// All use v_mfma_f32_32x32x16_bf16 in the transposed form of the forward:
 // the stationary operand (Q and dO, or K and V) sits in registers as the B
 // operand, streamed tiles are read from LDS row by row (A operand of the
 // score-like products) or through ds_read_b64_tr_b16 (A operand of the
 // accumulating products), and the P / dS fragments a lane computes are
-// already the B operand of the accumulating products.  Tiles are double
-// buffered in LDS through registers; P and dS are rounded to bf16 for the
-// matrix cores, everything else is fp32.
+// already the B operand of the accumulating products.  Tiles are staged in
+// LDS through registers; P and dS are rounded to bf16 for the matrix cores,
+// everything else is fp32.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
