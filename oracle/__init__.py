@@ -6,6 +6,7 @@ import this package.  The HIP library never uses it.
 from .oracle import (  # noqa: F401
     OracleLib,
     attn_bwd,
+    attn_bwd_rows,
     attn_fwd,
     attn_fwd_kv,
     attn_probs,

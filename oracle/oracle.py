@@ -68,6 +68,10 @@ class OracleLib:
         lib.tessera_oracle_attn_bwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
                                                 ctypes.c_double] + [_c_double_p] * 4
         lib.tessera_oracle_attn_bwd.restype = ctypes.c_int
+        lib.tessera_oracle_attn_bwd_rows.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
+                                                     ctypes.c_double, _c_int64_p, ctypes.c_int64,
+                                                     _c_int64_p, ctypes.c_int64] + [_c_double_p] * 4
+        lib.tessera_oracle_attn_bwd_rows.restype = ctypes.c_int
         lib.tessera_oracle_paged_decode.argtypes = [vp] * 5 + [ci] * 9 + [
             ctypes.c_double, _c_double_p, _c_double_p]
         lib.tessera_oracle_paged_decode.restype = ctypes.c_int
@@ -191,6 +195,30 @@ class OracleLib:
         self._check(rc, "tessera_oracle_attn_bwd")
         return dq, dk, dv, delta
 
+    def attn_bwd_rows(self, q, k, v, dout, causal: bool, scale: float, qrows, krows):
+        """The backward's dq and Delta of query rows `qrows` (flat index
+        (b*Hq + h)*T + i) and dk, dv of key rows `krows` (flat index
+        (b*Hkv + g)*T + j), each from the definitions.  Returns
+        (dq [nq,D], delta [nq], dk [nk,D], dv [nk,D]), fp64."""
+        (q, k, v), code, (B, Hq, Hkv, T, D) = self._prep(q, k, v)
+        dout = np.ascontiguousarray(dout)
+        if code != DTYPE_BF16 or dout.dtype != np.uint16 or dout.shape != q.shape:
+            raise ValueError("attn_bwd_rows takes bf16 patterns, dout shaped like q")
+        qrows = np.ascontiguousarray(qrows, dtype=np.int64)
+        krows = np.ascontiguousarray(krows, dtype=np.int64)
+        nq, nk = qrows.shape[0], krows.shape[0]
+        dq = np.empty((nq, D), np.float64)
+        delta = np.empty((nq,), np.float64)
+        dk = np.empty((nk, D), np.float64)
+        dv = np.empty((nk, D), np.float64)
+        rc = self.lib.tessera_oracle_attn_bwd_rows(
+            self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout), B, Hq, Hkv, T, D,
+            int(bool(causal)), float(scale), qrows.ctypes.data_as(_c_int64_p), nq,
+            krows.ctypes.data_as(_c_int64_p), nk,
+            *(a.ctypes.data_as(_c_double_p) for a in (dq, delta, dk, dv)))
+        self._check(rc, "tessera_oracle_attn_bwd_rows")
+        return dq, delta, dk, dv
+
     def paged_decode(self, q, k_cache, v_cache, block_table, context_lens, causal: bool,
                      scale: float):
         """Attention of the Tq newest query rows of each sequence over its K/V
@@ -255,6 +283,10 @@ def attn_probs(q, k, v, causal, scale):
 
 def attn_bwd(q, k, v, dout, causal, scale):
     return load().attn_bwd(q, k, v, dout, causal, scale)
+
+
+def attn_bwd_rows(q, k, v, dout, causal, scale, qrows, krows):
+    return load().attn_bwd_rows(q, k, v, dout, causal, scale, qrows, krows)
 
 
 def paged_decode(q, k_cache, v_cache, block_table, context_lens, causal, scale):

@@ -8,7 +8,10 @@
     heads (each softmax row sums to one); the dk rows add up to zero (softmax
     is unchanged by adding one vector to every key); Delta equals the row sums
     of dO * O with O from the forward oracle;
-  * GQA equals repeated-head MHA with dk, dv summed over the repeats.
+  * GQA equals repeated-head MHA with dk, dv summed over the repeats;
+  * the selected-rows entry (dq, Delta of chosen query rows, dk, dv of chosen
+    key rows, each rebuilt from the definitions) equals the rows of the full
+    call.
 """
 from __future__ import annotations
 
@@ -106,5 +109,19 @@ def pin_bwd_gqa_equals_repeated_mha(lib):
         assert np.abs(dv - mv.reshape(B, Hkv, G, T, D).sum(axis=2)).max() <= 1e-13
 
 
-ALL_BWD_PINS = [pin_bwd_torch_autograd, pin_bwd_finite_differences, pin_bwd_closed_forms,
-                pin_bwd_gqa_equals_repeated_mha]
+def pin_bwd_rows_entry(lib):
+    for causal in (True, False):
+        B, Hq, Hkv, T, D = 2, 6, 2, 37, 16
+        q, k, v, do = rand_bwd(B, Hq, Hkv, T, D, seed=61 + int(causal))
+        dq, dk, dv, delta = lib.attn_bwd(q, k, v, do, causal, 0.3)
+        qrows = np.array([0, 1, T - 1, T, 2 * T + 17, B * Hq * T - 1], np.int64)
+        krows = np.array([0, 5, T - 1, T + 3, 3 * T + 36, B * Hkv * T - 1], np.int64)
+        rq, rd, rk, rv = lib.attn_bwd_rows(q, k, v, do, causal, 0.3, qrows, krows)
+        assert np.abs(rq - dq.reshape(-1, D)[qrows]).max() <= 1e-12, causal
+        assert np.abs(rd - delta.reshape(-1)[qrows]).max() <= 1e-12, causal
+        assert np.abs(rk - dk.reshape(-1, D)[krows]).max() <= 1e-12, causal
+        assert np.abs(rv - dv.reshape(-1, D)[krows]).max() <= 1e-12, causal
+
+
+ALL_BWD_PINS = [pin_bwd_rows_entry, pin_bwd_torch_autograd, pin_bwd_finite_differences,
+                pin_bwd_closed_forms, pin_bwd_gqa_equals_repeated_mha]

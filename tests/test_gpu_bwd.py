@@ -125,3 +125,40 @@ def test_bwd_outlier_workload_slice():
                      f"mean {e.mean() / (MEAN_BAR * rms):.3f} of bar")
         assert e.max() <= MAX_BAR * top and e.mean() <= MEAN_BAR * rms, (name, e.max(), e.mean())
     say(" | ".join(stats))
+
+
+def test_bwd_long_context_sampled_rows():
+    """The long-context workload (B=1 Hq=32 Hkv=8 T=16384 D=128) at full size,
+    in the bench's launch: dq and Delta of 18 query rows (three heads, tile
+    edges and the ends) and dk, dv of 6 key rows of KV head 3, each rebuilt by
+    the oracle from the definitions.  The max-abs bar's scale, max|X|, is taken
+    over the whole GPU tensor (the oracle cannot afford all rows); the
+    mean-abs bar is a statistic of whole tensors and is left to the other
+    tests (these rows lean on the shortest rows, whose errors are largest)."""
+    w = inputs.WORKLOADS["t16384_d128"]
+    q, k, v = inputs.make_workload(w)
+    g = torch.Generator().manual_seed(7)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    say(f"case bwd workload {w.name}: {w.describe()}, sampled rows")
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    out, lse = binding.attn_fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    dq, dk, dv, delta = binding.attn_bwd(qd, kd, vd, out, lse, dod, causal=w.causal,
+                                         scale=w.scale)
+    torch.cuda.synchronize()
+    T = w.T
+    qrows = np.array([h * T + i for h in (0, 13, 31) for i in (0, 1, 63, 64, T // 2 - 1, T - 1)],
+                     np.int64)
+    krows = np.array([3 * T + j for j in (0, 1, 127, 128, 8000, T - 1)], np.int64)
+    rq, rd, rk, rv = oracle.attn_bwd_rows(inputs.bits(q), inputs.bits(k), inputs.bits(v),
+                                          inputs.bits(do), w.causal, w.scale, qrows, krows)
+    stats = []
+    for name, full, rows, ref in (("dq", dq, qrows, rq), ("delta", delta, qrows, rd),
+                                  ("dk", dk, krows, rk), ("dv", dv, krows, rv)):
+        f = full.float().cpu().numpy().astype(np.float64)
+        got = f.reshape(-1, w.D)[rows] if f.ndim == 4 else f.reshape(-1)[rows]
+        top = float(np.abs(f).max())
+        e = np.abs(got - ref)
+        stats.append(f"{name} max {e.max() / (MAX_BAR * top):.3f} of bar")
+        assert e.max() <= MAX_BAR * top, (name, e.max(), top)
+    say(" | ".join(stats))

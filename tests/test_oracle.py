@@ -83,6 +83,11 @@ BWD_MUTANTS = {
     "dp_from_keys": ("dot += wide(dout, qi + d) * wide(v,", "dot += wide(dout, qi + d) * wide(k,"),
     "mask_ignored": ("const int n = causal ? i + 1 : T;", "const int n = T;"),
     "unnormalised": ("s[j] /= Z;", "s[j] /= 1.0;"),
+    "rows_key_mask_shifted": ("for (int i = causal ? j : 0; i < T; ++i) {",
+                              "for (int i = causal ? j + 1 : 0; i < T; ++i) {"),
+    "rows_dv_without_p": ("ov[d] += p * wide(dout, qi + d);", "ov[d] += wide(dout, qi + d);"),
+    "rows_delta_unweighted": ("dl += exp(s[j] - lse) * dot;", "dl += dot;"),
+    "rows_dq_scale_dropped": ("o[d] += scale * ds * wide(k, kv0", "o[d] += ds * wide(k, kv0"),
 }
 
 
