@@ -47,12 +47,17 @@ constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kKeyTile = 64;              // keys per staged K/V tile
 constexpr int kPairedMinGrid = 2048;      // D = 64 grids that run two workgroups per CU
-// The running maximum m is only raised when some p = 2^(s*c - m) of a tile
-// would exceed 2^kRescaleSlack.  Any stale maximum gives the same result: it
-// cancels between the numerator and the row sum.  The bound keeps every p,
-// and the fp32 sums over up to 2^31 keys of p times |v| < 2^30, below the
-// fp32 range, and makes a raise rare once the first tile has set m.
-constexpr int kRescaleSlack = 64;
+// The running maximum m is lazy: P = 2^(s*c - m) is computed with the m in
+// hand, and m is only raised when some p of the tile reaches 2.  A raise sets
+// m to the tile max plus kHeadroom, so every p is then at most 2^-kHeadroom and
+// the next raise waits until a score exceeds that max by kHeadroom + 1 (log2
+// units).  Any stale m gives the same result: it cancels between the
+// numerator and the row sum.  Every p stays below 2, so the fp32 sums over up
+// to 2^31 keys cannot overflow, and the row's largest p stays at least
+// 2^-(kHeadroom+1), so the sums keep full precision.  The test needs no max:
+// p >= 2 exactly when bit 14 of its bf16 code is set, so one OR over the packed
+// P words decides it.
+constexpr int kHeadroom = 32;
 
 // LDS chunk swizzles (16-byte chunks of a D-wide bf16 row).  K is read as
 // 16-byte MFMA operands, one key row per lane; V is read with transposing
@@ -566,14 +571,12 @@ attn_fwd_bf16_kernel(Bf16Args a) {
                 if (r + 32 > last) s1[nb][i] = -INFINITY;
             }
         }
-        // Online softmax, in log2 units, with a lazy running max m.  P =
-        // 2^(s*c - m) is computed with the current m before the tile has been
-        // looked at; m only has to move when some p of the tile would exceed
-        // 2^kRescaleSlack, which the lane tests on its own tile max.  Any lane
-        // that asks for a move makes the whole wave take the branch, which
-        // takes the tile max over both lanes of each query row (so both keep
-        // the same m), rescales the accumulators and recomputes P.  Every p is
-        // at most 2^kRescaleSlack.  Tile 0 always takes the branch.
+        // Online softmax, in log2 units, with the lazy running max m (see
+        // kHeadroom).  P is computed and packed with the m in hand; if some p
+        // of the wave reached 2 (bit 14 of a bf16 code), the whole wave takes
+        // the branch, which raises m to the tile max over both lanes of each
+        // query row plus the headroom (so both keep the same m), rescales the
+        // accumulators and recomputes P.  Tile 0 takes the branch directly.
         f32x16 e0, e1;
         auto sweep = [&](float m_sub) __attribute__((always_inline)) {
 #pragma unroll
@@ -585,6 +588,18 @@ attn_fwd_bf16_kernel(Bf16Args a) {
             for (int i = 0; i < 16; ++i) {
                 e0[i] = __builtin_amdgcn_exp2f(e0[i]);
                 e1[i] = __builtin_amdgcn_exp2f(e1[i]);
+            }
+        };
+        // P to bf16, in the operand order of the P V MFMAs.
+        auto pack = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bf16x2 p0 =
+                    __builtin_convertvector((f32x2){e0[2 * e], e0[2 * e + 1]}, bf16x2);
+                const bf16x2 p1 =
+                    __builtin_convertvector((f32x2){e1[2 * e], e1[2 * e + 1]}, bf16x2);
+                pu[nb][e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p0);
+                pu[nb][2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
             }
         };
         auto own_max = [&]() __attribute__((always_inline)) {
@@ -599,10 +614,8 @@ attn_fwd_bf16_kernel(Bf16Args a) {
             }
             return fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])) * c;
         };
-        sweep(first ? 0.f : m_run[nb]);
-        const float m_own = own_max();
-        if (first || __builtin_amdgcn_ballot_w64(m_own > m_run[nb] + (float)kRescaleSlack) != 0) {
-            const float m_new = fmaxf(m_run[nb], max_with_partner(m_own));
+        auto raise = [&](float m_own) __attribute__((always_inline)) {
+            const float m_new = fmaxf(m_run[nb], max_with_partner(m_own) + (float)kHeadroom);
             const float alpha =
                 (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - m_new);
             lsum[nb][0] *= alpha;   // the two entries a lane may read
@@ -611,14 +624,30 @@ attn_fwd_bf16_kernel(Bf16Args a) {
             for (int db = 0; db < D / 32; ++db) acc[nb][db] *= alpha;
             m_run[nb] = m_new;
             sweep(m_new == -INFINITY ? 0.f : m_new);
-        }
-        // P to bf16, in the operand order of the P V MFMAs.
+        };
+        if (first) {
+            raise(own_max());
+            pack();
+        } else if constexpr (PAIRED) {
+            // The OR test keeps the scores live beside the packed P, which the
+            // 128-register build cannot afford; it tests its own tile max
+            // instead, and the scores die in the sweep when no raise follows.
+            sweep(m_run[nb]);
+            const float m_own = own_max();
+            if (__builtin_amdgcn_ballot_w64(m_own >= m_run[nb] + 1.f) != 0) raise(m_own);
+            pack();
+        } else {
+            sweep(m_run[nb]);
+            pack();
+            uint32_t any = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const bf16x2 p0 = __builtin_convertvector((f32x2){e0[2 * e], e0[2 * e + 1]}, bf16x2);
-            const bf16x2 p1 = __builtin_convertvector((f32x2){e1[2 * e], e1[2 * e + 1]}, bf16x2);
-            pu[nb][e >> 2][e & 3] = __builtin_bit_cast(uint32_t, p0);
-            pu[nb][2 + (e >> 2)][e & 3] = __builtin_bit_cast(uint32_t, p1);
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) any |= pu[nb][k][j];
+            if (__builtin_amdgcn_ballot_w64((any & 0x40004000u) != 0) != 0) {
+                raise(own_max());
+                pack();
+            }
         }
         }
     };

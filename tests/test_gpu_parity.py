@@ -133,20 +133,32 @@ def test_two_workgroups_per_cu_shapes(B, Hq, Hkv, T, D, causal):
     full_case(B, Hq, Hkv, T, D, "bf16", causal, seed=B + T)
 
 
-@pytest.mark.parametrize("D,rate,seed", [(64, 8.0, 5), (128, 8.0, 5), (128, 10.0, 7), (32, 10.0, 7)])
-def test_scores_growing_along_the_keys(D, rate, seed):
+# (D, rate, seed, B, Hq, Hkv, T, causal): the last two run the two-workgroups-
+# per-CU build (2048 workgroups) and the two-query-blocks-per-wave build.
+GROWING = [
+    (64, 8.0, 5, 1, 8, 2, 512, True),
+    (128, 8.0, 5, 1, 8, 2, 512, True),
+    (128, 10.0, 7, 1, 8, 2, 512, True),
+    (32, 10.0, 7, 1, 8, 2, 512, True),
+    (64, 2.0, 9, 128, 32, 8, 128, True),
+    (64, 8.0, 5, 1, 8, 2, 512, False),
+]
+
+
+@pytest.mark.parametrize("D,rate,seed,B,Hq,Hkv,T,causal", GROWING)
+def test_scores_growing_along_the_keys(D, rate, seed, B, Hq, Hkv, T, causal):
     """Key rows grow with position, so later tiles beat the running max by far
     more than the lazy-rescale bound: the rescale path runs mid-sequence.  The
     late rows attend almost entirely to one key, which is where a row sum of
     unrounded p against a P V product of rounded p would show."""
-    B, Hq, Hkv, T = 1, 8, 2, 512
     q, k, v = inputs.make_qkv(B, Hq, Hkv, T, D, "bf16", seed=seed)
     grow = (1.0 + torch.arange(T, dtype=torch.float32) / rate).view(1, 1, T, 1)
     k = (k.float() * grow).to(torch.bfloat16)
     scale = inputs.default_scale(D)
-    say(f"case growing keys B={B} Hq={Hq} Hkv={Hkv} T={T} D={D} rate={rate} seed={seed}")
-    o, l = run_gpu(q, k, v, True, scale)
-    O_ref, l_ref = oracle.attn_fwd(inputs.bits(q), inputs.bits(k), inputs.bits(v), True, scale)
+    say(f"case growing keys B={B} Hq={Hq} Hkv={Hkv} T={T} D={D} rate={rate} seed={seed} "
+        f"causal={causal}")
+    o, l = run_gpu(q, k, v, causal, scale)
+    O_ref, l_ref = oracle.attn_fwd(inputs.bits(q), inputs.bits(k), inputs.bits(v), causal, scale)
     check_close(o, l, O_ref, l_ref, "bf16")
     assert l_ref.max() - l_ref.min() > 64 * math.log(2)   # the spread that forces rescales
 
