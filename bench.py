@@ -203,7 +203,8 @@ def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the attention path here is single-GPU; see DESIGN.md for how it would shard)",
+              "(the attention path here runs on one GPU; more GPUs would each take a share "
+              "of the batch and KV heads in a process of their own)",
               file=sys.stderr)
         return 2
 
