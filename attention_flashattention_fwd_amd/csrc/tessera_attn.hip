@@ -53,10 +53,10 @@ constexpr int kPairedMinGrid = 2048;      // D = 64 grids that run two workgroup
 // the next raise waits until a score exceeds that max by kHeadroom + 1 (log2
 // units).  Any stale m gives the same result: it cancels between the
 // numerator and the row sum.  No p that reaches the matrix cores exceeds 2,
-// so the fp32 sums over up to 2^31 keys cannot overflow, and the row's largest p stays at least
-// 2^-(kHeadroom+1), so the sums keep full precision.  The test needs no max:
-// p >= 2 exactly when bit 14 of its bf16 code is set, so one OR over the packed
-// P words decides it.
+// so the fp32 sums over up to 2^31 keys cannot overflow, and the row's largest
+// p stays at least 2^-(kHeadroom+1), so the sums keep full precision.  The
+// test needs no max: p >= 2 exactly when bit 14 of its bf16 code is set, so one
+// OR over the packed P words decides it.
 constexpr int kHeadroom = 32;
 
 // LDS chunk swizzles (16-byte chunks of a D-wide bf16 row).  K is read as
