@@ -283,6 +283,23 @@ def make_qkv(B, Hq, Hkv, T, D, dtype="bf16", seed=0, outliers=""):
     return tuple(torch.from_numpy(a).to(tdt).contiguous() for a in arrs)
 
 
+def make_qkv_on_device(B, Hq, Hkv, T, D, seed, device):
+    """bf16 Q, K, V drawn on the GPU by torch's own seeded generator (Philox),
+    for sizes whose host draw would take minutes: N(0,1) in the order Q, K, V.
+    The draw is reproducible for a seed on one torch build; a test that uses
+    it hands the oracle slices copied back from these very tensors."""
+    return randn_on_device(((B, Hq, T, D), (B, Hkv, T, D), (B, Hkv, T, D)), seed, device)
+
+
+def randn_on_device(shapes, seed, device):
+    """bf16 N(0,1) tensors of the given shapes, drawn in order on the GPU by one
+    torch generator seeded with `seed`."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return tuple(torch.randn(shape, generator=g, device=device, dtype=torch.bfloat16)
+                 for shape in shapes)
+
+
 def make_workload(w: Workload):
     return make_qkv(w.B, w.Hq, w.Hkv, w.T, w.D, w.dtype, w.seed, w.outliers)
 

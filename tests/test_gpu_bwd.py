@@ -51,17 +51,23 @@ def run_case(B, Hq, Hkv, T, D, causal, seed, scale=None):
     torch.cuda.synchronize()
     r = oracle.attn_bwd(inputs.bits(q), inputs.bits(k), inputs.bits(v), inputs.bits(do), causal,
                         scale)
+    check_grads((dq, dk, dv, delta), r)
+
+
+def check_grads(got_all, ref_all, what=""):
+    """dq, dk, dv, Delta against the oracle's, each to the bar of its own
+    largest and RMS value."""
     stats = []
-    for name, got, ref in zip(("dq", "dk", "dv", "delta"), (dq, dk, dv, delta), r):
+    for name, got, ref in zip(("dq", "dk", "dv", "delta"), got_all, ref_all):
         g = got.float().cpu().numpy().astype(np.float64)
         assert np.isfinite(g).all(), name
         top, rms = float(np.abs(ref).max()), float(np.sqrt((ref ** 2).mean()))
         e = np.abs(g - ref)
         stats.append(f"{name} max {e.max():.2e} ({e.max() / max(top, 1e-30):.2%} of max) "
                      f"mean {e.mean():.2e} ({e.mean() / max(rms, 1e-30):.2%} of rms)")
-        assert e.max() <= MAX_BAR * top and e.mean() <= MEAN_BAR * rms, (name, e.max(),
+        assert e.max() <= MAX_BAR * top and e.mean() <= MEAN_BAR * rms, (name, what, e.max(),
                                                                             e.mean(), top, rms)
-    say(" | ".join(stats))
+    say(what, " | ".join(stats))
 
 
 CASES = [
@@ -162,3 +168,25 @@ def test_bwd_long_context_sampled_rows():
         stats.append(f"{name} max {e.max() / (MAX_BAR * top):.3f} of bar")
         assert e.max() <= MAX_BAR * top, (name, e.max(), top)
     say(" | ".join(stats))
+
+
+def test_bwd_offsets_past_int32():
+    """Q, dO, O and dq of 8200 x 32 x 128 x 64 elements (more than 2^31): the
+    last eight batch elements start past 2^31 elements.  Batch elements 0, 8192
+    and the last are compared whole against the oracle."""
+    B, Hq, Hkv, T, D = 8200, 32, 8, 128, 64
+    assert B * Hq * T * D > 2 ** 31
+    dev = torch.device("cuda:0")
+    say(f"case bwd int32-overflowing offsets B={B} Hq={Hq} Hkv={Hkv} T={T} D={D} causal")
+    q, k, v = inputs.make_qkv_on_device(B, Hq, Hkv, T, D, seed=22, device=dev)
+    (do,) = inputs.randn_on_device(((B, Hq, T, D),), seed=23, device=dev)
+    scale = inputs.default_scale(D)
+    out, lse = binding.attn_fwd(q, k, v, causal=True, scale=scale)
+    dq, dk, dv, delta = binding.attn_bwd(q, k, v, out, lse, do, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    for b in (0, 8192, B - 1):
+        sl = [t[b:b + 1].cpu() for t in (q, k, v, do)]
+        r = oracle.attn_bwd(*(inputs.bits(t) for t in sl), True, scale)
+        check_grads(tuple(t[b:b + 1] for t in (dq, dk, dv, delta)), r, f"batch element {b}")
+    del q, k, v, do, out, lse, dq, dk, dv, delta
+    torch.cuda.empty_cache()

@@ -165,3 +165,36 @@ def test_paged_serving_workload_sampled():
     O_ref, l_ref = oracle.paged_decode(inputs.bits(q[sub]), inputs.bits(kc), inputs.bits(vc),
                                        table.numpy()[sub], n[sub], w.causal, w.scale)
     check_paged(o[sub], l[sub], O_ref, l_ref, f"sequences {pick}")
+
+
+def test_paged_cache_offsets_past_int32():
+    """K/V caches of 140000 blocks x 8 KV heads x 16 x 128 elements (more than
+    2^31), with every table entry in the blocks past 2^31 elements.  The oracle
+    takes the same rows, gathered into a small cache under a renumbered table
+    (its answer does not depend on where blocks sit)."""
+    B, Hq, Hkv, Tq, D, bs, nblk, max_blocks = 2, 32, 8, 1, 128, 16, 140000, 64
+    first_high = 2 ** 31 // (Hkv * bs * D)                 # first block past 2^31 elements
+    assert nblk * Hkv * bs * D > 2 ** 31 and first_high == 131072
+    dev = torch.device("cuda:0")
+    say(f"case paged int32-overflowing cache offsets blocks={nblk} Hkv={Hkv} bs={bs} D={D}")
+    q, kc, vc = inputs.randn_on_device(((B, Hq, Tq, D), (nblk, Hkv, bs, D), (nblk, Hkv, bs, D)),
+                                       seed=24, device=dev)
+    lens = torch.tensor([700, max_blocks * bs], dtype=torch.int32)
+    rng = np.random.default_rng(24)
+    ids = rng.choice(np.arange(first_high, nblk), size=B * max_blocks, replace=False)
+    table = torch.from_numpy(ids.reshape(B, max_blocks).astype(np.int32))
+    scale = inputs.default_scale(D)
+    out, lse = binding.paged_decode(q, kc, vc, table.to(dev), lens.to(dev), causal=True,
+                                    scale=scale)
+    torch.cuda.synchronize()
+    used = torch.from_numpy(ids.astype(np.int64)).to(dev)
+    kc_small, vc_small = kc[used].cpu(), vc[used].cpu()
+    table_small = np.arange(B * max_blocks, dtype=np.int32).reshape(B, max_blocks)
+    O_ref, l_ref = oracle.paged_decode(inputs.bits(q.cpu()), inputs.bits(kc_small),
+                                       inputs.bits(vc_small), table_small, lens.numpy(), True,
+                                       scale)
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    check_paged(o, l, O_ref, l_ref, "high blocks")
+    del q, kc, vc, out, lse, used
+    torch.cuda.empty_cache()

@@ -163,6 +163,30 @@ def test_scores_growing_along_the_keys(D, rate, seed, B, Hq, Hkv, T, causal):
     assert l_ref.max() - l_ref.min() > 64 * math.log(2)   # the spread that forces rescales
 
 
+def test_offsets_past_int32():
+    """Q and O of 8200 x 32 x 128 x 64 elements (more than 2^31): the last
+    eight batch elements start past 2^31 elements, where any 32-bit element
+    or byte offset would wrap.  Those and batch element 0 are compared whole
+    against the oracle."""
+    B, Hq, Hkv, T, D = 8200, 32, 8, 128, 64
+    assert B * Hq * T * D > 2 ** 31 and 8192 * Hq * T * D == 2 ** 31
+    dev = torch.device("cuda:0")
+    say(f"case int32-overflowing offsets B={B} Hq={Hq} Hkv={Hkv} T={T} D={D} causal")
+    q, k, v = inputs.make_qkv_on_device(B, Hq, Hkv, T, D, seed=21, device=dev)
+    scale = inputs.default_scale(D)
+    out, lse = binding.attn_fwd(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    for b in (0, 8192, 8195, B - 1):
+        qs, ks, vs = (t[b:b + 1].cpu() for t in (q, k, v))
+        O_ref, l_ref = oracle.attn_fwd(inputs.bits(qs), inputs.bits(ks), inputs.bits(vs), True,
+                                       scale)
+        o = out[b:b + 1].float().cpu().numpy().astype(np.float64)
+        l = lse[b:b + 1].cpu().numpy().astype(np.float64)
+        check_close(o, l, O_ref, l_ref, "bf16", f"batch element {b}")
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("D,causal", [(32, True), (64, False), (128, True)])
 def test_identical_value_rows(dtype, D, causal):
