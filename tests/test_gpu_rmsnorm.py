@@ -95,3 +95,22 @@ def test_rmsnorm_benchmarked_workload(name):
     y = binding.rmsnorm_fwd(x.cuda(), w.cuda(), wl.eps)
     torch.cuda.synchronize()
     check(y, oracle.rmsnorm(inputs.bits(x), inputs.bits(w), float(np.float32(wl.eps))), name)
+
+
+def test_rmsnorm_offsets_past_int32():
+    """x and y of (2^19 + 8) x 4096 elements (more than 2^31): the last eight
+    rows start past 2^31 elements.  Those, the first and the row just before
+    the boundary are checked against the oracle."""
+    rows, n, eps = 2 ** 19 + 8, 4096, 1e-6
+    assert rows * n > 2 ** 31 and (2 ** 19) * n == 2 ** 31
+    dev = torch.device("cuda:0")
+    say(f"case rmsnorm int32-overflowing offsets rows={rows} n={n}")
+    x, w = inputs.randn_on_device(((rows, n), (n,)), seed=25, device=dev)
+    y = binding.rmsnorm_fwd(x, w, eps)
+    torch.cuda.synchronize()
+    pick = torch.tensor([0, 2 ** 19 - 1] + list(range(2 ** 19, rows)), device=dev)
+    xs, ys = x[pick].cpu(), y[pick]
+    check(ys, oracle.rmsnorm(inputs.bits(xs), inputs.bits(w.cpu()), float(np.float32(eps))),
+          "rows past 2^31 elements")
+    del x, y
+    torch.cuda.empty_cache()
