@@ -59,12 +59,23 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16-byte chunk swizzle of a D-wide bf16 row in LDS (keeps the row reads of
-// the MFMA A operand on distinct banks).
+// 16-byte chunk swizzle of a D-wide bf16 row in LDS, for tiles read both by
+// rows (16-byte A-operand reads) and transposed (ds_read_b64_tr_b16).  The LDS
+// serves 256 bytes a cycle: 16 lanes of a row read, or 16 lanes of a
+// transposed read (32 bytes of each of four consecutive rows).  Row reads stay
+// conflict-free when the swizzle permutes the chunks of the rows that share a
+// 256-byte window; transposed reads when the four rows' chunk pairs, XORed
+// with their swizzles, land apart, so the swizzles of those rows must differ
+// above bit 0.  D = 128 (one row per window): rows 4k..4k+3 take 0, 4, 8, 12
+// plus k % 4.  D = 64 (two rows per window, even and odd apart): rows 2m and
+// 2m+1 take 4 (m % 2) + (m / 2) % 4.  D = 32 (four rows per window): the
+// transposed rows already sit in different quarters.  Each is periodic in 16
+// rows, so the second 32-row block and the later 16-row steps are fixed
+// offsets.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-    if constexpr (D == 128) return row & 15;
-    else if constexpr (D == 64) return (row >> 1) & 7;
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
     else return (row >> 2) & 3;
 }
 
