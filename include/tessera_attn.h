@@ -63,7 +63,10 @@ enum tessera_attn_status {
 /*
  * bf16 attention forward.  q, k, v and out hold bfloat16 values (16-bit
  * patterns); products are accumulated in fp32 and out is rounded once to
- * bf16 (nearest even).  lse is fp32.  scale is any finite float (0 and
+ * bf16 (nearest even).  The softmax weights enter the P.V product as bf16,
+ * and the row sums that normalise out add those same rounded weights, so the
+ * weights of a row sum to one exactly as used.  lse is fp32 (natural log).
+ * scale is any finite float (0 and
  * negative values included); it multiplies q.k before the mask and softmax.
  * Returns a tessera_attn_status.
  */
