@@ -89,6 +89,10 @@ EDGE = [
     (1, 4, 4, 1000, 128, True),   # MHA, ragged, several tiles
     (2, 4, 1, 1000, 64, False),
     (1, 16, 4, 257, 32, True),
+    (1, 32, 1, 300, 128, True),   # G=32: eight head slots per KV head
+    (2, 10, 2, 150, 64, True),    # G=5: one head per workgroup
+    (1, 14, 2, 100, 32, False),   # G=7
+    (2, 8, 2, 777, 64, False),    # two query blocks per wave, ragged
 ]
 
 
