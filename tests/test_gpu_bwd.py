@@ -80,6 +80,9 @@ CASES = [
     (2, 8, 8, 64, 128, False),
     (1, 16, 4, 500, 64, True),
     (1, 12, 2, 130, 128, True),    # G = 6
+    (1, 16, 2, 200, 64, True),     # G = 8
+    (2, 10, 2, 150, 128, False),   # G = 5, ragged, no mask
+    (1, 32, 1, 96, 32, True),      # G = 32
 ]
 
 
