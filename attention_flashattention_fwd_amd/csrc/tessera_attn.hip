@@ -20,6 +20,7 @@
 #include <string.h>
 
 #include "tessera_attn.h"
+#include "launch.h"
 
 #define TESSERA_VERSION 10200
 
@@ -867,12 +868,6 @@ int validate(const void *q, const void *k, const void *v, const void *out, const
     return TESSERA_OK;
 }
 
-int launch_status(void) {
-    const hipError_t e = hipGetLastError();
-    if (e == hipSuccess) return TESSERA_OK;
-    snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
-    return TESSERA_ERR_LAUNCH;
-}
 
 // Query blocks of 32 rows per wave.  Two for D = 64 without the causal mask:
 // every K/V operand read from LDS then feeds two MFMAs and a phase holds as
@@ -919,21 +914,20 @@ int launch_bf16(const void *q, const void *k, const void *v, void *out, float *l
     // that land together are too uneven in length (causal tiles differ).
     const bool paired = grid >= kPairedMinGrid && !ragged;
     if (D == 128) {
-        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true, false, 1>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false, false, 1>), g, blk, 0, s, a);
+        if (ragged) return tessera_launch(attn_fwd_bf16_kernel<128, true, false, 1>, g, blk, s, a);
+        else return tessera_launch(attn_fwd_bf16_kernel<128, false, false, 1>, g, blk, s, a);
     } else if (D == 64 && nq == 2) {
-        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true, false, 2>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false, false, 2>), g, blk, 0, s, a);
+        if (ragged) return tessera_launch(attn_fwd_bf16_kernel<64, true, false, 2>, g, blk, s, a);
+        else return tessera_launch(attn_fwd_bf16_kernel<64, false, false, 2>, g, blk, s, a);
     } else if (D == 64 && paired) {
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false, true, 1>), g, blk, 0, s, a);
+        return tessera_launch(attn_fwd_bf16_kernel<64, false, true, 1>, g, blk, s, a);
     } else if (D == 64) {
-        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true, false, 1>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false, false, 1>), g, blk, 0, s, a);
+        if (ragged) return tessera_launch(attn_fwd_bf16_kernel<64, true, false, 1>, g, blk, s, a);
+        else return tessera_launch(attn_fwd_bf16_kernel<64, false, false, 1>, g, blk, s, a);
     } else {
-        if (ragged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<32, true, false, 1>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<32, false, false, 1>), g, blk, 0, s, a);
+        if (ragged) return tessera_launch(attn_fwd_bf16_kernel<32, true, false, 1>, g, blk, s, a);
+        return tessera_launch(attn_fwd_bf16_kernel<32, false, false, 1>, g, blk, s, a);
     }
-    return launch_status();
 }
 
 }  // namespace
@@ -963,16 +957,15 @@ extern "C" int tessera_attn_fwd_f32(const float *q, const float *k, const float 
     const int64_t grid = (int64_t)ntiles * B * Hq;
     if (grid > 0x7fffffff) return TESSERA_ERR_TOO_LARGE;
     hipStream_t s = (hipStream_t)stream;
+    const dim3 g((unsigned)grid), blk(256);
     if (D == 128)
-        hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, q, k, v,
-                           out, lse, Hq, Hkv, T, ntiles, causal, scale);
-    else if (D == 64)
-        hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, q, k, v,
-                           out, lse, Hq, Hkv, T, ntiles, causal, scale);
-    else
-        hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, dim3((unsigned)grid), dim3(256), 0, s, q, k, v,
-                           out, lse, Hq, Hkv, T, ntiles, causal, scale);
-    return launch_status();
+        return tessera_launch(attn_fwd_f32_kernel<128>, g, blk, s, q, k, v, out, lse, Hq, Hkv, T,
+                              ntiles, causal, scale);
+    if (D == 64)
+        return tessera_launch(attn_fwd_f32_kernel<64>, g, blk, s, q, k, v, out, lse, Hq, Hkv, T,
+                              ntiles, causal, scale);
+    return tessera_launch(attn_fwd_f32_kernel<32>, g, blk, s, q, k, v, out, lse, Hq, Hkv, T,
+                          ntiles, causal, scale);
 }
 
 extern "C" const char *tessera_attn_status_string(int status) {
@@ -999,7 +992,11 @@ extern "C" const char *tessera_attn_status_string(int status) {
 
 extern "C" const char *tessera_attn_last_error(void) { return g_last_error; }
 
-// The launch check of this file, for the library's other sources (not exported).
-__attribute__((visibility("hidden"))) int tessera_launch_status(void) { return launch_status(); }
+// The launch result of every entry point of the library (not exported).
+__attribute__((visibility("hidden"))) int tessera_launch_result(hipError_t e) {
+    if (e == hipSuccess) return TESSERA_OK;
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    return TESSERA_ERR_LAUNCH;
+}
 
 extern "C" int tessera_attn_version(void) { return TESSERA_VERSION; }

@@ -36,8 +36,8 @@
 #include <stdint.h>
 
 #include "tessera_attn.h"
+#include "launch.h"
 
-int tessera_launch_status(void);   // tessera_attn.hip
 
 namespace {
 
@@ -762,15 +762,16 @@ extern "C" int tessera_attn_bwd(const void *q, const void *k, const void *v, con
     hipStream_t s = (hipStream_t)stream;
     const dim3 g1((unsigned)grid_dq), b1(64 * a.dq_waves), g2((unsigned)grid_kv), b2(kKvThreads);
     // dq first: it writes the Delta rows the dk/dv kernel reads.
+    int st;
     if (D == 128) {
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, g1, b1, 0, s, a);
-        hipLaunchKernelGGL(attn_bwd_dkdv_lag_kernel<128>, g2, b2, 0, s, a);
+        st = tessera_launch(attn_bwd_dq_kernel<128>, g1, b1, s, a);
+        if (st == TESSERA_OK) st = tessera_launch(attn_bwd_dkdv_lag_kernel<128>, g2, b2, s, a);
     } else if (D == 64) {
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, g1, b1, 0, s, a);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, g2, b2, 0, s, a);
+        st = tessera_launch(attn_bwd_dq_kernel<64>, g1, b1, s, a);
+        if (st == TESSERA_OK) st = tessera_launch(attn_bwd_dkdv_kernel<64>, g2, b2, s, a);
     } else {
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<32>, g1, b1, 0, s, a);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<32>, g2, b2, 0, s, a);
+        st = tessera_launch(attn_bwd_dq_kernel<32>, g1, b1, s, a);
+        if (st == TESSERA_OK) st = tessera_launch(attn_bwd_dkdv_kernel<32>, g2, b2, s, a);
     }
-    return tessera_launch_status();
+    return st;
 }

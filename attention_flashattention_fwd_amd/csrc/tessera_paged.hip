@@ -33,8 +33,7 @@
 #include <stdint.h>
 
 #include "tessera_paged.h"
-
-int tessera_launch_status(void);   // tessera_attn.hip
+#include "launch.h"
 
 namespace {
 
@@ -603,15 +602,13 @@ extern "C" int tessera_paged_decode(const void *q, const void *k_cache, const vo
 
     hipStream_t sm = (hipStream_t)stream;
     const dim3 grid((unsigned)((int64_t)p.nsplit * B * Hkv)), blk(64);
-    if (D == 128) hipLaunchKernelGGL(paged_decode_kernel<128>, grid, blk, 0, sm, a);
-    else if (D == 64) hipLaunchKernelGGL(paged_decode_kernel<64>, grid, blk, 0, sm, a);
-    else hipLaunchKernelGGL(paged_decode_kernel<32>, grid, blk, 0, sm, a);
-    st = tessera_launch_status();
+    if (D == 128) st = tessera_launch(paged_decode_kernel<128>, grid, blk, sm, a);
+    else if (D == 64) st = tessera_launch(paged_decode_kernel<64>, grid, blk, sm, a);
+    else st = tessera_launch(paged_decode_kernel<32>, grid, blk, sm, a);
     if (st != TESSERA_OK || p.nsplit <= 1) return st;
     const int64_t nrows = (int64_t)rows;
     const dim3 cgrid((unsigned)((nrows + 3) / 4)), cblk(256);
-    if (D == 128) hipLaunchKernelGGL(paged_combine_kernel<128>, cgrid, cblk, 0, sm, a, nrows);
-    else if (D == 64) hipLaunchKernelGGL(paged_combine_kernel<64>, cgrid, cblk, 0, sm, a, nrows);
-    else hipLaunchKernelGGL(paged_combine_kernel<32>, cgrid, cblk, 0, sm, a, nrows);
-    return tessera_launch_status();
+    if (D == 128) return tessera_launch(paged_combine_kernel<128>, cgrid, cblk, sm, a, nrows);
+    if (D == 64) return tessera_launch(paged_combine_kernel<64>, cgrid, cblk, sm, a, nrows);
+    return tessera_launch(paged_combine_kernel<32>, cgrid, cblk, sm, a, nrows);
 }

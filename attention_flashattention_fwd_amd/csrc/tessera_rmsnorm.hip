@@ -20,8 +20,7 @@
 #include <stdint.h>
 
 #include "tessera_rmsnorm.h"
-
-int tessera_launch_status(void);   // tessera_attn.hip
+#include "launch.h"
 
 namespace {
 
@@ -150,22 +149,21 @@ extern "C" int tessera_rmsnorm_fwd(const void *x, const void *w, void *y, long l
     const float inv_n = 1.f / (float)n;
     const int64_t nrows = rows;
     if (nvec <= 64)
-        hipLaunchKernelGGL(rmsnorm_reg_kernel<1>, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
-                           eps);
+        return tessera_launch(rmsnorm_reg_kernel<1>, g, blk, s, xv, wv, yv, nrows, nvec, inv_n,
+                              eps);
     else if (nvec <= 128)
-        hipLaunchKernelGGL(rmsnorm_reg_kernel<2>, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
-                           eps);
+        return tessera_launch(rmsnorm_reg_kernel<2>, g, blk, s, xv, wv, yv, nrows, nvec, inv_n,
+                              eps);
     else if (nvec <= 256)
-        hipLaunchKernelGGL(rmsnorm_reg_kernel<4>, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
-                           eps);
+        return tessera_launch(rmsnorm_reg_kernel<4>, g, blk, s, xv, wv, yv, nrows, nvec, inv_n,
+                              eps);
     else if (nvec <= 512)
-        hipLaunchKernelGGL(rmsnorm_reg_kernel<8>, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
-                           eps);
+        return tessera_launch(rmsnorm_reg_kernel<8>, g, blk, s, xv, wv, yv, nrows, nvec, inv_n,
+                              eps);
     else if (nvec <= kRegMaxVec)
-        hipLaunchKernelGGL(rmsnorm_reg_kernel<16>, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
-                           eps);
+        return tessera_launch(rmsnorm_reg_kernel<16>, g, blk, s, xv, wv, yv, nrows, nvec, inv_n,
+                              eps);
     else
-        hipLaunchKernelGGL(rmsnorm_stream_kernel, g, blk, 0, s, xv, wv, yv, nrows, nvec, inv_n,
-                           eps);
-    return tessera_launch_status();
+        return tessera_launch(rmsnorm_stream_kernel, g, blk, s, xv, wv, yv, nrows, nvec, inv_n,
+                              eps);
 }
