@@ -23,16 +23,30 @@ def test_defaults_fit_the_contract():
 
 def test_recorded_traffic_needs_the_current_source(tmp_path, monkeypatch):
     """A counter summary is used only when it names the current kernel source."""
-    summary = tmp_path / "traffic.md"
-    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", summary)
-    assert bench.recorded_traffic() == (None, None)
+    monkeypatch.setattr(bench, "PROFILES", tmp_path)
+    summary = bench.traffic_summary("t16384_d128")
+    assert summary.parent == tmp_path
+    assert bench.recorded_traffic("t16384_d128") == (None, None)
     summary.write_text("    kernel_source_sha256_16: 0000000000000000\n"
                        "    hbm_bytes_per_launch: 1.5e8\n")
-    assert bench.recorded_traffic() == (None, None)
+    assert bench.recorded_traffic("t16384_d128") == (None, None)
     summary.write_text(f"    kernel_source_sha256_16: {bench.source_digest()}\n"
                        "    hbm_bytes_per_launch: 1.5e8\n    mfma_busy_pct: 80.5\n")
-    traffic, extra = bench.recorded_traffic()
+    traffic, extra = bench.recorded_traffic("t16384_d128")
     assert traffic == 1.5e8 and extra == {"mfma_busy_pct": 80.5}
+    assert bench.recorded_traffic("t4096_outliers") == (None, None)
+
+
+def test_every_forward_workload_is_benchmarked():
+    from attention_flashattention_fwd_amd import inputs
+    lines = {bench.HEADLINE, *bench.SECONDARY}
+    assert set(inputs.WORKLOADS) | set(inputs.KV_WORKLOADS) == lines
+
+
+def test_markers_work_without_a_profiler():
+    m = bench.Markers()
+    m.push("test range")
+    m.pop()
 
 
 def test_source_digest_ignores_comments(tmp_path, monkeypatch):

@@ -254,21 +254,8 @@ def test_binding_argument_checks():
                          k[..., :48].contiguous())
 
 
-# -- the full-size workloads: sampled rows + whole-tensor properties --------
-def sample_rows(B, Hq, T, n_rand, seed):
-    rng = np.random.default_rng(seed)
-    fixed_i = sorted({0, 1, 31, 32, 63, 64, 65, 127, 128, T // 2, T - 65, T - 64, T - 2, T - 1})
-    heads = [(0, 0), (B - 1, Hq - 1), (B // 2, Hq // 2), (0, Hq - 1)]
-    rows = [(b * Hq + h) * T + i for b, h in heads for i in fixed_i if 0 <= i < T]
-    rows += list(rng.integers(0, B * Hq * T, n_rand))
-    return np.unique(np.array(rows, np.int64))
-
-
-@pytest.mark.parametrize("name", ["t2048", "t2048_full", "t4096_outliers",
-                                  "t4096_outlier_rows", "t16384_d128"])
-def test_full_size_workload(name):
-    w = inputs.WORKLOADS[name]
-    say(f"workload {name}: {w.describe()}")
+# -- the full-size workloads, in the launch configuration the bench times ----
+def gpu_workload(w):
     q, k, v = inputs.make_workload(w)
     dev = torch.device("cuda:0")
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
@@ -281,10 +268,43 @@ def test_full_size_workload(name):
         assert torch.equal(out[:, :, 0], vd[:, :, 0].repeat_interleave(G, dim=1))
         s0 = (qd[:, :, 0].float() * kd[:, :, 0].float().repeat_interleave(G, dim=1)).sum(-1)
         assert torch.allclose(lse[:, :, 0], s0 * w.scale, atol=1e-3, rtol=0)
-    rows = sample_rows(w.B, w.Hq, w.T, 400, seed=len(name))
-    say(f"oracle on {len(rows)} sampled rows")
+    return q, k, v, out, lse
+
+
+@pytest.mark.parametrize("name", ["t2048", "t2048_full", "t4096_outliers",
+                                  "t4096_outlier_rows"])
+def test_full_size_workload_every_element(name):
+    """T=2048 (causal and not) and T=4096 (both outlier readings) at full size:
+    every element of out and lse against the oracle."""
+    w = inputs.WORKLOADS[name]
+    say(f"workload {name}: {w.describe()}, every element")
+    q, k, v, out, lse = gpu_workload(w)
+    O_ref, l_ref = oracle.attn_fwd(inputs.bits(q), inputs.bits(k), inputs.bits(v), w.causal,
+                                   w.scale)
+    check_close(out.float().cpu().numpy().astype(np.float64),
+                lse.cpu().numpy().astype(np.float64), O_ref, l_ref, w.dtype, name)
+
+
+def test_full_size_long_context_whole_groups():
+    """The long-context workload (B=1 Hq=32 Hkv=8 T=16384 D=128) at full size:
+    every element of out and lse of two whole GQA groups, KV heads 0 and 7
+    with their query heads 0-3 and 28-31, against the oracle; the other
+    groups are checked on 400 random rows."""
+    w = inputs.WORKLOADS["t16384_d128"]
+    say(f"workload {w.name}: {w.describe()}, KV heads 0 and 7 whole")
+    q, k, v, out, lse = gpu_workload(w)
+    G = w.Hq // w.Hkv
+    for g in (0, w.Hkv - 1):
+        hs = slice(g * G, (g + 1) * G)
+        O_ref, l_ref = oracle.attn_fwd(inputs.bits(q[:, hs]), inputs.bits(k[:, g:g + 1]),
+                                       inputs.bits(v[:, g:g + 1]), w.causal, w.scale)
+        check_close(out[:, hs].float().cpu().numpy().astype(np.float64),
+                    lse[:, hs].cpu().numpy().astype(np.float64), O_ref, l_ref, w.dtype,
+                    f"KV head {g}")
+    rows = np.unique(np.random.default_rng(5).integers(0, w.B * w.Hq * w.T, 400)).astype(np.int64)
     O_ref, l_ref = oracle.attn_rows(inputs.bits(q), inputs.bits(k), inputs.bits(v), w.causal,
                                     w.scale, rows)
-    o = out.reshape(-1, w.D)[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
-    l = lse.reshape(-1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
-    check_close(o.astype(np.float64), l.astype(np.float64), O_ref, l_ref, w.dtype, name)
+    idx = torch.from_numpy(rows).to(out.device)
+    o = out.reshape(-1, w.D)[idx].float().cpu().numpy().astype(np.float64)
+    l = lse.reshape(-1)[idx].cpu().numpy().astype(np.float64)
+    check_close(o, l, O_ref, l_ref, w.dtype, "random rows")
