@@ -30,10 +30,12 @@ ERR_TOO_LARGE = 8
 ERR_LAUNCH = 9
 ERR_EPS = 10
 ERR_WORKSPACE = 11
+ERR_SCRATCH = 12
 
 EXPORTS = ("tessera_attn_fwd", "tessera_attn_fwd_kv", "tessera_attn_fwd_f32", "tessera_attn_bwd",
            "tessera_attn_status_string", "tessera_attn_last_error", "tessera_attn_version",
-           "tessera_rmsnorm_fwd", "tessera_paged_decode", "tessera_paged_decode_workspace")
+           "tessera_rmsnorm_fwd", "tessera_paged_decode", "tessera_paged_decode_workspace",
+           "tessera_paged_decode_noalloc", "tessera_paged_decode_scratch_limit")
 
 _lib = None
 
@@ -66,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.tessera_paged_decode.argtypes = [vp] * 7 + [i] * 9 + [f, vp, ctypes.c_longlong, vp]
         L.tessera_paged_decode.restype = i
         L.tessera_paged_decode_workspace.argtypes = [i] * 7
+        L.tessera_paged_decode_noalloc.argtypes = [vp] * 7 + [i] * 9 + [f, vp]
+        L.tessera_paged_decode_noalloc.restype = i
+        L.tessera_paged_decode_scratch_limit.argtypes = []
+        L.tessera_paged_decode_scratch_limit.restype = ctypes.c_longlong
         L.tessera_paged_decode_workspace.restype = ctypes.c_longlong
         L.tessera_attn_status_string.argtypes = [i]
         L.tessera_attn_status_string.restype = ctypes.c_char_p
@@ -317,6 +323,22 @@ def raw_paged(q, kc, vc, table, lens, out, lse, B, Hq, Hkv, Tq, D, num_blocks, b
                                           float(np.float32(scale)), ws, int(ws_bytes), stream))
 
 
+def raw_paged_noalloc(q, kc, vc, table, lens, out, lse, B, Hq, Hkv, Tq, D, num_blocks,
+                      block_size, max_blocks, causal, scale, stream) -> int:
+    """Call tessera_paged_decode_noalloc with integer device addresses; returns
+    the status."""
+    return int(lib().tessera_paged_decode_noalloc(q, kc, vc, table, lens, out, lse, int(B),
+                                                  int(Hq), int(Hkv), int(Tq), int(D),
+                                                  int(num_blocks), int(block_size),
+                                                  int(max_blocks), int(causal),
+                                                  float(np.float32(scale)), stream))
+
+
+def paged_scratch_limit() -> int:
+    """Bytes of the library's fixed scratch behind tessera_paged_decode_noalloc."""
+    return int(lib().tessera_paged_decode_scratch_limit())
+
+
 def _check_paged(q, k_cache, v_cache, block_table, context_lens):
     import torch
 
@@ -382,6 +404,40 @@ def paged_decode_into(q, k_cache, v_cache, block_table, context_lens, out, lse, 
         if st == ERR_LAUNCH:
             msg += ": " + lib().tessera_attn_last_error().decode()
         raise RuntimeError(f"tessera_paged_decode failed ({st}): {msg}")
+
+
+def paged_decode_noalloc_into(q, k_cache, v_cache, block_table, context_lens, out, lse,
+                              causal: bool = True, scale: float | None = None,
+                              stream=None) -> None:
+    """paged_decode_into without a workspace: tessera_paged_decode_noalloc,
+    whose split partials use the library's fixed per-GPU scratch buffer, so
+    neither this call nor the library allocates.  Calls on one GPU must not
+    overlap in time (they share that buffer)."""
+    import torch
+
+    B, Hq, Hkv, Tq, D, nblk, bs, maxb = _check_paged(q, k_cache, v_cache, block_table,
+                                                      context_lens)
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32 or lse.device != q.device \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Tq] on q's device")
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = raw_paged_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                               block_table.data_ptr(), context_lens.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, Hq, Hkv, Tq, D, nblk, bs, maxb,
+                               int(bool(causal)), scale, handle)
+    if st != OK:
+        msg = status_string(st)
+        if st == ERR_LAUNCH:
+            msg += ": " + lib().tessera_attn_last_error().decode()
+        raise RuntimeError(f"tessera_paged_decode_noalloc failed ({st}): {msg}")
 
 
 def paged_decode(q, k_cache, v_cache, block_table, context_lens, causal: bool = True,

@@ -19,8 +19,8 @@ __attribute__((visibility("hidden"))) int tessera_launch_result(hipError_t e);
 // converted to the kernel's parameter type and held here until
 // hipLaunchKernel has copied it.
 template <typename... P, typename... A>
-inline int tessera_launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
-                          A... args) {
+__attribute__((visibility("hidden"))) inline int
+tessera_launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A... args) {
     static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
     std::tuple<P...> held{static_cast<P>(args)...};
     return std::apply(

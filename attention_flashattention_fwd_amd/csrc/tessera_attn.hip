@@ -986,6 +986,10 @@ extern "C" const char *tessera_attn_status_string(int status) {
     case TESSERA_ERR_LAUNCH: return "HIP kernel launch failed";
     case TESSERA_ERR_EPS: return "eps must be finite and non-negative";
     case TESSERA_ERR_WORKSPACE: return "workspace missing or smaller than required";
+    case TESSERA_ERR_SCRATCH:
+        return "the split partials of this decode exceed the library's fixed scratch buffer "
+               "(tessera_paged_decode_scratch_limit bytes); pass a workspace to "
+               "tessera_paged_decode instead";
     default: return "unknown status";
     }
 }

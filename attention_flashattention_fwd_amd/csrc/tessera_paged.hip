@@ -32,6 +32,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "tessera_paged.h"
 #include "launch.h"
 
@@ -538,12 +541,60 @@ extern "C" long long tessera_paged_decode_workspace(int B, int Hq, int Hkv, int 
     return workspace_bytes_for(B, Hq, Hkv, Tq, D, make_plan(B, Hkv, block_size, max_blocks));
 }
 
-extern "C" int tessera_paged_decode(const void *q, const void *k_cache, const void *v_cache,
-                                    const int *block_table, const int *context_lens, void *out,
-                                    float *lse, int B, int Hq, int Hkv, int Tq, int D,
-                                    int num_blocks, int block_size, int max_blocks, int causal,
-                                    float scale, void *workspace, long long workspace_bytes,
-                                    void *stream) {
+// ---------------------------------------------------------------------------
+// The decode without a caller workspace: the split partials go to `scratch`, a
+// fixed buffer of the library in each GPU's memory (every GPU the library runs
+// on holds its own copy until the process ends).  In host code the array's
+// name is only a stand-in for it; the device address of the current GPU's
+// copy is looked up once per device with hipGetSymbolAddress and kept, and
+// only that address is ever handed to a kernel.  Calls on one GPU share the
+// buffer: two of them that overlap in time (other streams, other threads)
+// race on it.  Its contents on entry do not matter (every cell the merge
+// reads is written by the split kernel of the same call), so nothing clears
+// it.
+// ---------------------------------------------------------------------------
+constexpr long long kScratchBytes = 32ll << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The device address of the current GPU's scratch, looked up on first use.
+int scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return tessera_launch_result(e);
+    if (dev < 0 || dev >= kMaxDevices) return TESSERA_ERR_UNSUPPORTED;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e == hipSuccess && !p) e = hipErrorInvalidSymbol;
+            if (e != hipSuccess) return tessera_launch_result(e);
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return TESSERA_OK;
+}
+
+// The body of both decode entry points: checks, then the two launches.
+// With use_scratch, the library's scratch buffer of the current GPU takes the
+// place of the caller's workspace (which is then ignored), looked up only
+// once every argument has passed its checks.
+int paged_decode(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
+                 const int *context_lens, void *out, float *lse, int B, int Hq, int Hkv, int Tq,
+                 int D, int num_blocks, int block_size, int max_blocks, int causal, float scale,
+                 void *workspace, long long workspace_bytes, bool use_scratch, void *stream) {
+    if (use_scratch) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+    }
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out || !lse)
         return TESSERA_ERR_NULL;
     if (num_blocks < 1) return TESSERA_ERR_SHAPE;
@@ -558,12 +609,14 @@ extern "C" int tessera_paged_decode(const void *q, const void *k_cache, const vo
         return TESSERA_ERR_ALIGN;
     const Plan p = make_plan(B, Hkv, block_size, max_blocks);
     const int64_t need = workspace_bytes_for(B, Hq, Hkv, Tq, D, p);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return TESSERA_ERR_WORKSPACE;
+    if (use_scratch && need > kScratchBytes) return TESSERA_ERR_SCRATCH;
+    if (!use_scratch && need > 0 && (!workspace || workspace_bytes < need))
+        return TESSERA_ERR_WORKSPACE;
     const size_t rows = (size_t)B * Hq * Tq;
     const size_t qbytes = rows * D * 2, lbytes = rows * 4;
     const size_t cbytes = (size_t)num_blocks * Hkv * block_size * D * 2;
     const size_t tbytes = (size_t)B * max_blocks * 4, nbytes = (size_t)B * 4;
-    const size_t wbytes = (size_t)need;
+    const size_t wbytes = workspace ? (size_t)need : 0;   // the library scratch: no overlap
     const void *ins[5] = {q, k_cache, v_cache, block_table, context_lens};
     const size_t insz[5] = {qbytes, cbytes, cbytes, tbytes, nbytes};
     for (int i = 0; i < 5; ++i)
@@ -573,6 +626,10 @@ extern "C" int tessera_paged_decode(const void *q, const void *k_cache, const vo
     if (overlaps(out, qbytes, lse, lbytes) || overlaps(out, qbytes, workspace, wbytes) ||
         overlaps(lse, lbytes, workspace, wbytes))
         return TESSERA_ERR_ALIAS;
+    if (use_scratch && need > 0) {
+        st = scratch_of_current_device(&workspace);
+        if (st != TESSERA_OK) return st;
+    }
 
     PagedArgs a;
     a.q = (const uint16_t *)q;
@@ -611,4 +668,30 @@ extern "C" int tessera_paged_decode(const void *q, const void *k_cache, const vo
     if (D == 128) return tessera_launch(paged_combine_kernel<128>, cgrid, cblk, sm, a, nrows);
     if (D == 64) return tessera_launch(paged_combine_kernel<64>, cgrid, cblk, sm, a, nrows);
     return tessera_launch(paged_combine_kernel<32>, cgrid, cblk, sm, a, nrows);
+}
+
+}  // namespace
+
+extern "C" int tessera_paged_decode(const void *q, const void *k_cache, const void *v_cache,
+                                    const int *block_table, const int *context_lens, void *out,
+                                    float *lse, int B, int Hq, int Hkv, int Tq, int D,
+                                    int num_blocks, int block_size, int max_blocks, int causal,
+                                    float scale, void *workspace, long long workspace_bytes,
+                                    void *stream) {
+    return paged_decode(q, k_cache, v_cache, block_table, context_lens, out, lse, B, Hq, Hkv, Tq,
+                        D, num_blocks, block_size, max_blocks, causal, scale, workspace,
+                        workspace_bytes, false, stream);
+}
+
+extern "C" long long tessera_paged_decode_scratch_limit(void) { return kScratchBytes; }
+
+extern "C" int tessera_paged_decode_noalloc(const void *q, const void *k_cache,
+                                            const void *v_cache, const int *block_table,
+                                            const int *context_lens, void *out, float *lse, int B,
+                                            int Hq, int Hkv, int Tq, int D, int num_blocks,
+                                            int block_size, int max_blocks, int causal,
+                                            float scale, void *stream) {
+    return paged_decode(q, k_cache, v_cache, block_table, context_lens, out, lse, B, Hq, Hkv, Tq,
+                        D, num_blocks, block_size, max_blocks, causal, scale, nullptr, 0, true,
+                        stream);
 }

@@ -57,7 +57,9 @@ enum tessera_attn_status {
     TESSERA_ERR_TOO_LARGE = 8,   /* the launch grid would exceed 2^31 - 1 workgroups */
     TESSERA_ERR_LAUNCH = 9,      /* the HIP kernel launch failed */
     TESSERA_ERR_EPS = 10,        /* RMSNorm eps is NaN, infinite or negative */
-    TESSERA_ERR_WORKSPACE = 11   /* paged decode workspace NULL or too small */
+    TESSERA_ERR_WORKSPACE = 11,  /* paged decode workspace NULL or too small */
+    TESSERA_ERR_SCRATCH = 12     /* the allocation-free paged decode needs more than the
+                                    library's fixed scratch buffer holds */
 };
 
 /*

@@ -77,6 +77,29 @@ int tessera_paged_decode(const void *q, const void *k_cache, const void *v_cache
                          int max_blocks, int causal, float scale, void *workspace,
                          long long workspace_bytes, void *stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as tessera_paged_decode, with the same arguments except the
+ * workspace, and identical results.  The split partials go to a fixed
+ * scratch buffer of tessera_paged_decode_scratch_limit() bytes (32 MiB) that
+ * the library holds in each GPU's memory from its first use on that GPU until
+ * the process ends; the call itself allocates nothing.  Sizes whose workspace
+ * (tessera_paged_decode_workspace) exceeds that limit return
+ * TESSERA_ERR_SCRATCH with nothing launched.  Every call on one GPU uses
+ * that GPU's one buffer: calls that overlap in time on one GPU (other
+ * streams or threads) race on it, so the caller serialises them, for
+ * example by issuing them on one stream.
+ */
+int tessera_paged_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                 const int *block_table, const int *context_lens, void *out,
+                                 float *lse, int B, int Hq, int Hkv, int Tq, int D,
+                                 int num_blocks, int block_size, int max_blocks, int causal,
+                                 float scale, void *stream);
+
+/* Bytes of the fixed scratch buffer behind tessera_paged_decode_noalloc. */
+long long tessera_paged_decode_scratch_limit(void);
+
 #ifdef __cplusplus
 }
 #endif

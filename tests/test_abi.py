@@ -35,7 +35,7 @@ def test_library_loads_and_exports_every_symbol():
 
 
 def test_status_strings():
-    for code in range(0, 12):
+    for code in range(0, 13):
         assert binding.status_string(code)
     assert binding.status_string(123) == "unknown status"
     assert binding.lib().tessera_attn_last_error() == b""
@@ -202,3 +202,35 @@ def call_paged(q=Q, kc=KC, vc=VC, bt=BT, cl=CL, o=O, l=L, B=2, Hq=8, Hkv=2, Tq=2
 ])
 def test_paged_bad_arguments_are_rejected_before_launch(kwargs, code):
     assert call_paged(**kwargs) == code
+
+
+def call_paged_noalloc(q=Q, kc=KC, vc=VC, bt=BT, cl=CL, o=O, l=L, B=2, Hq=8, Hkv=2, Tq=2, D=64,
+                       num_blocks=64, block_size=16, max_blocks=100, causal=1, scale=0.125):
+    return binding.raw_paged_noalloc(q, kc, vc, bt, cl, o, l, B, Hq, Hkv, Tq, D, num_blocks,
+                                     block_size, max_blocks, causal, scale, None)
+
+
+def test_paged_noalloc_scratch_limit():
+    assert binding.paged_scratch_limit() == 32 << 20
+    # the serving batch of the bench (64 sequences of up to 16384 tokens) fits
+    assert 0 < binding.raw_paged_workspace(64, 32, 8, 1, 128, 16, 1024) <= 32 << 20
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(bt=None), binding.ERR_NULL),
+    (dict(o=None), binding.ERR_NULL),
+    (dict(num_blocks=0), binding.ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), binding.ERR_SHAPE),
+    (dict(D=96), binding.ERR_UNSUPPORTED),
+    (dict(block_size=8), binding.ERR_UNSUPPORTED),
+    (dict(causal=2), binding.ERR_CAUSAL),
+    (dict(scale=float("inf")), binding.ERR_SCALE),
+    (dict(kc=KC + 8), binding.ERR_ALIGN),
+    (dict(o=KC + 4096), binding.ERR_ALIAS),
+    # partials of 64 x 32 query rows over 64 splits: 68 MB of workspace > 32 MiB
+    (dict(B=64, Hq=32, Hkv=8, Tq=1, D=128, max_blocks=4096), binding.ERR_SCRATCH),
+])
+def test_paged_noalloc_bad_arguments_are_rejected_before_launch(kwargs, code):
+    # every check, the scratch limit included, comes before any HIP call
+    assert call_paged_noalloc(**kwargs) == code
+    assert "scratch" in binding.status_string(binding.ERR_SCRATCH)
