@@ -14,10 +14,12 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
-#include <utility>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
+
+#include <mutex>
+#include <utility>
 
 #include "tessera_attn.h"
 #include "launch.h"
@@ -92,7 +94,35 @@ struct Bf16Args {
     int causal;
     int qmode;    // 0: q as given, 1: q negated (scale < 0), 2: q zeroed (scale == 0)
     float c;      // |scale| * log2(e)  (1 when scale == 0)
+    int nitems;   // work items: query tiles x (KV head, head slot) pairs
+    uint32_t *queue;   // work queues of a persistent launch, or null (one item per workgroup)
 };
+
+// Persistent launches.  The chip's XCDs do not run at one speed (in one
+// measurement the slowest took 6 % longer per tile than the fastest), and a
+// plain grid hands each XCD a fixed share of the items (workgroup i runs on
+// XCD i mod 8), so the slowest XCD finishes last while the others idle.  A
+// persistent launch instead keeps one workgroup per free slot and lets each
+// pull items from a queue: queue x holds the items i = x mod 8 in order,
+// which is the set and the order (longest causal tile first) that XCD x would
+// get from a plain grid, so its K/V rows stay in that XCD's L2.  A workgroup
+// starts with the queue of its own XCD; once that queue is empty it takes the
+// next item of the other queues, which by then are the shortest ones.  The
+// queue heads, a count of items handed out and a count of finished workgroups
+// live in a small block of device memory (kQueueWords words, one 128-byte
+// line per counter); the last workgroup to finish sets them back to zero for
+// the next launch.  A persistent launch pays an atomic round trip per item and
+// its workgroups cannot overlap one item's end with the next one's start, so
+// it is used only where each slot gets several items (kPersistMinItems).
+constexpr int kQueues = 8;
+constexpr int kTicket = kQueues;                       // counter of items handed out
+constexpr int kDone = kQueues + 1;                     // counter of finished workgroups
+constexpr int kCounters = kQueues + 2;
+constexpr int kQueueStride = 32;                       // words between counters
+constexpr int kQueueWords = kCounters * kQueueStride;
+// The kernel arguments in the kernel-argument (constant) address space, so
+// that reads of them stay scalar loads.
+typedef const __attribute__((address_space(4))) Bf16Args *ArgsPtr;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -459,24 +489,23 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, uint32_t vrel,
 // vector phases of one overlap the matrix-core phases of the other on top of
 // the ping-pong inside each: the vector work of a single wave is bound by its
 // own issue rate, and two waves issuing it side by side go about twice as fast.
-template <int D, bool RAGGED, bool PAIRED, int NQ>
-__global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(PAIRED ? 4 : 2)))
-attn_fwd_bf16_kernel(Bf16Args a) {
-    static_assert(!PAIRED || (D == 64 && !RAGGED), "two workgroups per CU: D = 64, Tk % 64 == 0");
-    static_assert(NQ == 1 || (D == 64 && !PAIRED), "two query blocks per wave: D = 64, one workgroup per CU");
-    __shared__ LdsRing<D> lds;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+//
+// attn_fwd_bf16_item is one work item: the query tile, KV head and head slot
+// of `item`, from the prologue loads to the stores of out and lse.
+template <int D, bool RAGGED, bool PAIRED, int NQ, bool PERSIST, class Args>
+__device__ __forceinline__ void attn_fwd_bf16_item(Args &a, LdsRing<D> &lds, int item) {
+    // In a persistent workgroup the lane index is opaque, so that nothing
+    // derived from it is hoisted out of the loop over items and held across
+    // items.
+    const int lane = PERSIST ? lane_id_opaque() : (int)(threadIdx.x & 63);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const bool lag = w >= 4;      // the half that runs one phase behind
     const int hi = lane >> 5;     // which half of the wave
     const int col = lane & 31;    // query column of this lane
 
     const int per_tile = a.nbh * a.nslots;
-    const int qt_rev = blockIdx.x / per_tile;
-    const int rem = blockIdx.x - qt_rev * per_tile;
+    const int qt_rev = item / per_tile;
+    const int rem = item - qt_rev * per_tile;
     const int qt = a.causal ? (a.nqt - 1 - qt_rev) : qt_rev;
     const int slot = rem / a.nbh;
     const int bh = rem - slot * a.nbh;                // b * Hkv + kv head
@@ -761,6 +790,75 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     }
 }
 
+// A plain launch: one workgroup per item, item blockIdx.x.
+template <int D, bool RAGGED, bool PAIRED, int NQ>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(PAIRED ? 4 : 2)))
+attn_fwd_bf16_kernel(Bf16Args a) {
+    static_assert(!PAIRED || (D == 64 && !RAGGED), "two workgroups per CU: D = 64, Tk % 64 == 0");
+    static_assert(NQ == 1 || (D == 64 && !PAIRED), "two query blocks per wave: D = 64, one workgroup per CU");
+    __shared__ LdsRing<D> lds;
+    attn_fwd_bf16_item<D, RAGGED, PAIRED, NQ, false>(a, lds, (int)blockIdx.x);
+}
+
+// A persistent launch: each workgroup takes items from the queues until every
+// queue is empty.
+template <int D, bool RAGGED, bool PAIRED, int NQ>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(PAIRED ? 4 : 2)))
+attn_fwd_bf16_persistent_kernel(Bf16Args args) {
+    __shared__ LdsRing<D> lds;
+    __shared__ int s_item;
+
+    const int tid = threadIdx.x;
+    uint32_t *const queue = args.queue;
+    // Thread 0: the queue it starts with (its XCD's, from the XCC_ID hardware
+    // register) and the queues found empty.
+    const int home = (int)(__builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & (kQueues - 1));
+    uint32_t empty = 0;
+    for (;;) {
+        // The barrier also keeps the next item's loads into LDS behind every
+        // wave's last read of the previous item.
+        // A ticket below nitems entitles the workgroup to one item, which one
+        // of the queues still holds (as many tickets as items are handed out);
+        // a later ticket means every item is taken, found with one access.
+        if (tid == 0) {
+            int it = -1;
+            if ((int)atomicAdd(queue + kTicket * kQueueStride, 1u) < args.nitems) {
+                for (int t = 0; t < kQueues && it < 0; ++t) {
+                    const int x = (home + t) & (kQueues - 1);
+                    if ((empty >> x) & 1u) continue;
+                    const int len = (args.nitems - x + kQueues - 1) / kQueues;
+                    const int k = (int)atomicAdd(queue + x * kQueueStride, 1u);
+                    if (k < len) it = x + kQueues * k;
+                    else empty |= 1u << x;
+                }
+            }
+            s_item = it;
+        }
+        __syncthreads();
+        const int item = __builtin_amdgcn_readfirstlane(s_item);
+        if (item < 0) break;
+        // The arguments are read afresh from the kernel-argument segment for
+        // every item (through an opaque pointer), so that neither they nor
+        // anything derived from them is held in registers across items.
+        ArgsPtr ap = (ArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ap));
+        attn_fwd_bf16_item<D, RAGGED, PAIRED, NQ, true>(*ap, lds, item);
+    }
+
+    // The last workgroup to finish resets the queues.  Every other one has
+    // made its last queue access before it counts itself done, so no access
+    // to the counters can follow the reset.
+    if (tid == 0) {
+        __threadfence();
+        const uint32_t done = atomicAdd(queue + kDone * kQueueStride, 1u);
+        if (done == gridDim.x - 1) {
+            for (int x = 0; x < kCounters; ++x) atomicExch(queue + x * kQueueStride, 0u);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 kernel (vector ALUs): 64 query rows per workgroup, four lanes per row,
 // each lane owning D/4 interleaved dims; K/V tiles staged in LDS.
@@ -879,6 +977,89 @@ int query_blocks_per_wave(int D, int causal) {
     return (D == 64 && !causal) ? 2 : 1;
 }
 
+// ---------------------------------------------------------------------------
+// Work queues of persistent launches: kQueueSlots blocks of kQueueWords
+// counters per GPU, zero from the library's load on.  A stream keeps one
+// block for all its calls: calls on one stream run one after another, so a
+// block is never used by two launches at once.  Calls on other streams use
+// other blocks; past kQueueSlots streams on one device, and while a stream is
+// being captured into a graph (whose replays could overlap), launches run as
+// plain grids, which need no counters.
+// ---------------------------------------------------------------------------
+constexpr int kQueueSlots = 64;
+constexpr int kMaxDevices = 64;
+constexpr int kPersistMinItems = 4;   // items per workgroup slot for a persistent launch
+
+}  // namespace
+
+__device__ __align__(128) uint32_t g_work_queues[kQueueSlots * kQueueWords];
+
+namespace {
+
+struct DeviceQueues {
+    uint32_t *base = nullptr;            // device address of g_work_queues on this GPU
+    int cus = 0;                         // compute units
+    int nslots = 0;
+    void *stream[kQueueSlots] = {};      // the stream that owns each block
+};
+std::mutex g_queues_mutex;
+DeviceQueues g_queues[kMaxDevices];
+
+// The counter block of `stream` on the current GPU and the GPU's compute-unit
+// count, or null when no block is free (or the lookup failed).
+uint32_t *queue_block(hipStream_t stream, int *cus) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+        return nullptr;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_queues_mutex);
+    DeviceQueues &d = g_queues[dev];
+    if (d.base == nullptr) {
+        void *p = nullptr;
+        int n = 0;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_work_queues)) != hipSuccess || p == nullptr ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 1)
+            return nullptr;
+        d.base = (uint32_t *)p;
+        d.cus = n;
+    }
+    *cus = d.cus;
+    for (int i = 0; i < d.nslots; ++i)
+        if (d.stream[i] == (void *)stream) return d.base + (size_t)i * kQueueWords;
+    if (d.nslots == kQueueSlots) return nullptr;
+    d.stream[d.nslots] = (void *)stream;
+    return d.base + (size_t)(d.nslots++) * kQueueWords;
+}
+
+// Launches the bf16 build <D, RAGGED, PAIRED, NQ> over `items` work items: as
+// a persistent grid (one workgroup per slot the GPU holds at once, items from
+// the queues) when there are more items than slots, else one workgroup per
+// item.
+template <int D, bool RAGGED, bool PAIRED, int NQ>
+int launch_items(Bf16Args a, int64_t items, hipStream_t s) {
+    a.nitems = (int)items;
+    a.queue = nullptr;
+    int cus = 0;
+    // The two-workgroups-per-CU build has no persistent form: the work loop
+    // pushes it past its 128 registers.
+    uint32_t *q = PAIRED ? nullptr : queue_block(s, &cus);
+    if (q != nullptr) {
+        auto *persistent = attn_fwd_bf16_persistent_kernel<D, RAGGED, false, NQ>;
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)persistent,
+                                                         kThreads, 0) == hipSuccess &&
+            per_cu > 0 && items >= (int64_t)kPersistMinItems * per_cu * cus) {
+            a.queue = q;
+            return tessera_launch(persistent, dim3((unsigned)(per_cu * cus)), dim3(kThreads), s,
+                                  a);
+        }
+    }
+    return tessera_launch(attn_fwd_bf16_kernel<D, RAGGED, PAIRED, NQ>, dim3((unsigned)items),
+                          dim3(kThreads), s, a);
+}
+
 // The bf16 launch shared by both entry points (arguments already validated).
 int launch_bf16(const void *q, const void *k, const void *v, void *out, float *lse, int B,
                 int Hq, int Hkv, int Tq, int Tk, int D, int causal, float scale, void *stream) {
@@ -907,26 +1088,25 @@ int launch_bf16(const void *q, const void *k, const void *v, void *out, float *l
     a.c = scale == 0.f ? 1.0f : (float)(fabs((double)scale) * kLog2e);
 
     hipStream_t s = (hipStream_t)stream;
-    const dim3 g((unsigned)grid), blk(kThreads);
     const bool ragged = Tk % kKeyTile != 0;
     // Two workgroups per CU pay off once the grid covers the 512 slots of 256
     // CUs several times over; on a grid that fills them about once, the pairs
     // that land together are too uneven in length (causal tiles differ).
     const bool paired = grid >= kPairedMinGrid && !ragged;
     if (D == 128) {
-        if (ragged) return tessera_launch(attn_fwd_bf16_kernel<128, true, false, 1>, g, blk, s, a);
-        else return tessera_launch(attn_fwd_bf16_kernel<128, false, false, 1>, g, blk, s, a);
+        if (ragged) return launch_items<128, true, false, 1>(a, grid, s);
+        return launch_items<128, false, false, 1>(a, grid, s);
     } else if (D == 64 && nq == 2) {
-        if (ragged) return tessera_launch(attn_fwd_bf16_kernel<64, true, false, 2>, g, blk, s, a);
-        else return tessera_launch(attn_fwd_bf16_kernel<64, false, false, 2>, g, blk, s, a);
+        if (ragged) return launch_items<64, true, false, 2>(a, grid, s);
+        return launch_items<64, false, false, 2>(a, grid, s);
     } else if (D == 64 && paired) {
-        return tessera_launch(attn_fwd_bf16_kernel<64, false, true, 1>, g, blk, s, a);
+        return launch_items<64, false, true, 1>(a, grid, s);
     } else if (D == 64) {
-        if (ragged) return tessera_launch(attn_fwd_bf16_kernel<64, true, false, 1>, g, blk, s, a);
-        else return tessera_launch(attn_fwd_bf16_kernel<64, false, false, 1>, g, blk, s, a);
+        if (ragged) return launch_items<64, true, false, 1>(a, grid, s);
+        return launch_items<64, false, false, 1>(a, grid, s);
     } else {
-        if (ragged) return tessera_launch(attn_fwd_bf16_kernel<32, true, false, 1>, g, blk, s, a);
-        return tessera_launch(attn_fwd_bf16_kernel<32, false, false, 1>, g, blk, s, a);
+        if (ragged) return launch_items<32, true, false, 1>(a, grid, s);
+        return launch_items<32, false, false, 1>(a, grid, s);
     }
 }
 

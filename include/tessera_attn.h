@@ -29,12 +29,24 @@
  * keeps every buffer alive until then.  `out` and `lse` must not overlap
  * q, k, v or each other.
  *
+ * Work queues.  A bf16 call with at least four work items (query tiles times
+ * KV heads) per workgroup the GPU holds at once runs as a persistent launch:
+ * its workgroups pull items from queues, so that the GPU's dies, which do not
+ * all run at one speed, finish together.  The queue counters live in a small
+ * block of device memory that belongs to the library (part of its loaded
+ * code, zero at load; every such launch leaves it at zero again).  Each
+ * stream gets a block of its own on its first such call, up to 64 streams
+ * per device; calls on further streams, and calls on a stream that is being
+ * captured into a graph, run as plain grids without counters.  Results are
+ * the same bits either way.
+ *
  * Errors.  Every argument is checked before anything is enqueued; a failed
  * check returns its status with no buffer touched and nothing launched.
  * TESSERA_ERR_LAUNCH means the HIP launch itself failed; the HIP error text
  * is then available from tessera_attn_last_error() on the calling thread.
  * No C++ exception crosses this interface and nothing is printed.
- * The functions hold no state and may be called from several threads.
+ * The functions may be called from several threads; the only state they keep
+ * is the stream-to-queue-block table above, updated under a lock.
  */
 #ifndef TESSERA_ATTN_H
 #define TESSERA_ATTN_H

@@ -137,6 +137,56 @@ def test_two_workgroups_per_cu_shapes(B, Hq, Hkv, T, D, causal):
     full_case(B, Hq, Hkv, T, D, "bf16", causal, seed=B + T)
 
 
+# Grids with at least four work items (query tile x KV head x head slot) per
+# workgroup the GPU holds at once run as persistent launches that take items
+# from per-XCD queues.  Each case below has more than 1024 items (four per CU
+# on 256 CUs); every element is compared, and repeated calls on one stream and
+# calls on two streams at once must give the same bits (each launch resets
+# its queue counters, which are kept per stream).
+PERSISTENT = [
+    (8, 16, 4, 2112, 128, True),   # 1056 items
+    (8, 16, 4, 2100, 128, True),   # ragged
+    (8, 16, 4, 2112, 64, True),    # one workgroup per CU at D = 64
+    (8, 16, 4, 2100, 64, True),    # ragged
+    (128, 8, 8, 300, 64, False),   # two query blocks per wave, 1024 items
+    (4, 32, 8, 2100, 32, True),    # 1056 items
+    (128, 8, 8, 64, 128, True),    # 1024 one-tile items
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D,causal", PERSISTENT)
+def test_persistent_launch_shapes(B, Hq, Hkv, T, D, causal):
+    q, k, v, o, l = full_case(B, Hq, Hkv, T, D, "bf16", causal, seed=T + B)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    outs = [binding.attn_fwd(qd, kd, vd, causal=causal) for _ in range(3)]
+    torch.cuda.synchronize()
+    ref_o = torch.from_numpy(o).to(torch.bfloat16)
+    for out, lse in outs:
+        assert torch.equal(out.cpu(), ref_o) and np.array_equal(lse.cpu().numpy(), l)
+
+
+def test_persistent_launches_on_two_streams():
+    B, Hq, Hkv, T, D = 8, 16, 4, 2112, 128
+    q1, k1, v1 = (t.cuda() for t in inputs.make_qkv(B, Hq, Hkv, T, D, "bf16", seed=41))
+    q2, k2, v2 = (t.cuda() for t in inputs.make_qkv(B, Hq, Hkv, T, D, "bf16", seed=42))
+    want1 = binding.attn_fwd(q1, k1, v1)
+    want2 = binding.attn_fwd(q2, k2, v2)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    got = []
+    for _ in range(3):
+        o1, l1 = torch.empty_like(q1), torch.empty_like(want1[1])
+        o2, l2 = torch.empty_like(q2), torch.empty_like(want2[1])
+        binding.attn_fwd_into(q1, k1, v1, o1, l1, True, None, stream=s1)
+        binding.attn_fwd_into(q2, k2, v2, o2, l2, True, None, stream=s2)
+        got.append((o1, l1, o2, l2))
+    torch.cuda.synchronize()
+    for o1, l1, o2, l2 in got:
+        assert torch.equal(o1, want1[0]) and torch.equal(l1, want1[1])
+        assert torch.equal(o2, want2[0]) and torch.equal(l2, want2[1])
+
+
 # (D, rate, seed, B, Hq, Hkv, T, causal): the last two run the two-workgroups-
 # per-CU build (2048 workgroups) and the two-query-blocks-per-wave build.
 GROWING = [
