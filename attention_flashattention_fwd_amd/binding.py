@@ -35,7 +35,22 @@ ERR_SCRATCH = 12
 EXPORTS = ("tessera_attn_fwd", "tessera_attn_fwd_kv", "tessera_attn_fwd_f32", "tessera_attn_bwd",
            "tessera_attn_status_string", "tessera_attn_last_error", "tessera_attn_version",
            "tessera_rmsnorm_fwd", "tessera_paged_decode", "tessera_paged_decode_workspace",
-           "tessera_paged_decode_noalloc", "tessera_paged_decode_scratch_limit")
+           "tessera_paged_decode_noalloc", "tessera_paged_decode_scratch_limit",
+           "tessera_attn_fwd_tile_config", "tessera_attn_fwd_with_config")
+
+
+class TileConfig(ctypes.Structure):
+    """tessera_attn_tile_config (include/tessera_attn.h)."""
+    _fields_ = [("heads_per_workgroup", ctypes.c_int), ("query_rows_per_wave", ctypes.c_int),
+                ("workgroups_per_cu", ctypes.c_int), ("persistent", ctypes.c_int)]
+
+    def as_tuple(self):
+        return (self.heads_per_workgroup, self.query_rows_per_wave, self.workgroups_per_cu,
+                self.persistent)
+
+    def __repr__(self):
+        return ("TileConfig(heads_per_workgroup={}, query_rows_per_wave={}, "
+                "workgroups_per_cu={}, persistent={})".format(*self.as_tuple()))
 
 _lib = None
 
@@ -70,6 +85,11 @@ def lib() -> ctypes.CDLL:
         L.tessera_paged_decode_workspace.argtypes = [i] * 7
         L.tessera_paged_decode_noalloc.argtypes = [vp] * 7 + [i] * 9 + [f, vp]
         L.tessera_paged_decode_noalloc.restype = i
+        L.tessera_attn_fwd_tile_config.argtypes = [i] * 7 + [ctypes.POINTER(TileConfig)]
+        L.tessera_attn_fwd_tile_config.restype = i
+        L.tessera_attn_fwd_with_config.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
+                                                   ctypes.POINTER(TileConfig), vp]
+        L.tessera_attn_fwd_with_config.restype = i
         L.tessera_paged_decode_scratch_limit.argtypes = []
         L.tessera_paged_decode_scratch_limit.restype = ctypes.c_longlong
         L.tessera_paged_decode_workspace.restype = ctypes.c_longlong
@@ -103,6 +123,55 @@ def raw_fwd_kv(q, k, v, out, lse, B, Hq, Hkv, Tq, Tk, D, causal, scale, stream) 
     return int(lib().tessera_attn_fwd_kv(q, k, v, out, lse, int(B), int(Hq), int(Hkv), int(Tq),
                                          int(Tk), int(D), int(causal),
                                          float(np.float32(scale)), stream))
+
+
+def tile_config(B, Hq, Hkv, Tq, Tk, D, causal) -> TileConfig:
+    """The tile configuration the library's table picks for these sizes."""
+    c = TileConfig()
+    st = int(lib().tessera_attn_fwd_tile_config(int(B), int(Hq), int(Hkv), int(Tq), int(Tk),
+                                                int(D), int(causal), ctypes.byref(c)))
+    if st != OK:
+        raise RuntimeError(f"tessera_attn_fwd_tile_config failed ({st}): {status_string(st)}")
+    return c
+
+
+def raw_fwd_with_config(q, k, v, out, lse, B, Hq, Hkv, Tq, Tk, D, causal, scale, config,
+                        stream) -> int:
+    """Call tessera_attn_fwd_with_config with integer device addresses and a
+    TileConfig (or None); returns the status."""
+    ptr = ctypes.byref(config) if config is not None else None
+    return int(lib().tessera_attn_fwd_with_config(q, k, v, out, lse, int(B), int(Hq), int(Hkv),
+                                                  int(Tq), int(Tk), int(D), int(causal),
+                                                  float(np.float32(scale)), ptr, stream))
+
+
+def attn_fwd_with_config_into(q, k, v, out, lse, config: TileConfig, causal: bool = True,
+                              scale: float | None = None, stream=None) -> None:
+    """attn_fwd_kv_into with an explicit tile configuration (bfloat16 only)."""
+    import torch
+
+    B, Hq, Hkv, Tq, D = _check_inputs(q, k, v, same_rows=False)
+    Tk = k.shape[2]
+    if q.dtype != torch.bfloat16:
+        raise ValueError("attn_fwd_with_config takes bfloat16 q, k, v")
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, Tq]")
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = raw_fwd_with_config(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), B, Hq, Hkv, Tq, Tk, D, int(bool(causal)), scale,
+                                 config, handle)
+    if st != OK:
+        msg = status_string(st)
+        if st == ERR_LAUNCH:
+            msg += ": " + lib().tessera_attn_last_error().decode()
+        raise RuntimeError(f"tessera_attn_fwd_with_config failed ({st}): {msg}")
 
 
 def _check_inputs(q, k, v, same_rows: bool = True):

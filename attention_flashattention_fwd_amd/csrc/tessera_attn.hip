@@ -49,7 +49,6 @@ constexpr double kLog2e = 1.442695040888963407;
 constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kKeyTile = 64;              // keys per staged K/V tile
-constexpr int kPairedMinGrid = 2048;      // D = 64 grids that run two workgroups per CU
 // The running maximum m is lazy: P = 2^(s*c - m) is computed with the m in
 // hand, and m is only raised when some p of the tile reaches 2.  A raise sets
 // m to the tile max plus kHeadroom, so every p is then at most 2^-kHeadroom and
@@ -795,8 +794,8 @@ template <int D, bool RAGGED, bool PAIRED, int NQ>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(PAIRED ? 4 : 2)))
 attn_fwd_bf16_kernel(Bf16Args a) {
-    static_assert(!PAIRED || (D == 64 && !RAGGED), "two workgroups per CU: D = 64, Tk % 64 == 0");
-    static_assert(NQ == 1 || (D == 64 && !PAIRED), "two query blocks per wave: D = 64, one workgroup per CU");
+    static_assert(!PAIRED || (D <= 64 && !RAGGED), "two workgroups per CU: D <= 64, Tk % 64 == 0");
+    static_assert(NQ == 1 || (D <= 64 && !PAIRED), "64 rows per wave: D <= 64, one workgroup per CU");
     __shared__ LdsRing<D> lds;
     attn_fwd_bf16_item<D, RAGGED, PAIRED, NQ, false>(a, lds, (int)blockIdx.x);
 }
@@ -967,14 +966,56 @@ int validate(const void *q, const void *k, const void *v, const void *out, const
 }
 
 
-// Query blocks of 32 rows per wave.  Two for D = 64 without the causal mask:
-// every K/V operand read from LDS then feeds two MFMAs and a phase holds as
-// many MFMAs as at D = 128, so the per-phase barriers and reads cost half as
-// much per flop (7 % faster at T = 2048).  Under the causal mask the query
-// tiles twice as tall waste more work on the diagonal, and the two-workgroups
-// per CU build is faster there.
-int query_blocks_per_wave(int D, int causal) {
-    return (D == 64 && !causal) ? 2 : 1;
+// ---------------------------------------------------------------------------
+// Tile configurations (tessera_attn_tile_config) and the static table of the
+// library's picks.
+// ---------------------------------------------------------------------------
+struct TileRule {
+    int D, causal, large, heads_per_workgroup, query_rows_per_wave, workgroups_per_cu, persistent;
+};
+#include "tile_table.inc"
+
+constexpr int kLargeRowsPerCu = 1024;   // problem-size class boundary of the table
+constexpr int kDefaultCus = 256;        // MI355X, when the device cannot be asked
+
+int compute_units() {
+    int dev = -1, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n > 0)
+        return n;
+    return kDefaultCus;
+}
+
+// The table's configuration for these sizes, fitted to them: the largest head
+// grouping up to the rule's that divides the GQA group, and one workgroup per
+// CU when the key count is not a multiple of the key tile.
+tessera_attn_tile_config table_config(int B, int Hq, int Hkv, int Tq, int Tk, int D, int causal) {
+    const int64_t rows_per_cu = (int64_t)B * Hq * Tq / compute_units();
+    const int large = rows_per_cu >= kLargeRowsPerCu ? 1 : 0;
+    tessera_attn_tile_config c = {4, 32, 1, 0};
+    for (const TileRule &r : kTileTable) {
+        if (r.D == D && r.causal == causal && r.large == large) {
+            c = {r.heads_per_workgroup, r.query_rows_per_wave, r.workgroups_per_cu, r.persistent};
+            break;
+        }
+    }
+    const int G = Hq / Hkv;
+    while (G % c.heads_per_workgroup != 0) c.heads_per_workgroup /= 2;
+    if (Tk % kKeyTile != 0) c.workgroups_per_cu = 1;
+    return c;
+}
+
+// Whether configuration c is one these sizes allow (see the header).
+bool config_allowed(const tessera_attn_tile_config &c, int Hq, int Hkv, int Tk, int D) {
+    const int hg = c.heads_per_workgroup;
+    if ((hg != 1 && hg != 2 && hg != 4) || (Hq / Hkv) % hg != 0) return false;
+    if (c.query_rows_per_wave != 32 && c.query_rows_per_wave != 64) return false;
+    if (c.workgroups_per_cu != 1 && c.workgroups_per_cu != 2) return false;
+    if (c.persistent != 0 && c.persistent != 1) return false;
+    if (c.query_rows_per_wave == 64 && (D > 64 || c.workgroups_per_cu == 2)) return false;
+    if (c.workgroups_per_cu == 2 && (D > 64 || Tk % kKeyTile != 0 || c.persistent)) return false;
+    return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -1035,34 +1076,54 @@ uint32_t *queue_block(hipStream_t stream, int *cus) {
 
 // Launches the bf16 build <D, RAGGED, PAIRED, NQ> over `items` work items: as
 // a persistent grid (one workgroup per slot the GPU holds at once, items from
-// the queues) when there are more items than slots, else one workgroup per
-// item.
+// the queues) when asked for and there are more items than slots, else one
+// workgroup per item.
 template <int D, bool RAGGED, bool PAIRED, int NQ>
-int launch_items(Bf16Args a, int64_t items, hipStream_t s) {
+int launch_items(Bf16Args a, int64_t items, bool persistent, hipStream_t s) {
     a.nitems = (int)items;
     a.queue = nullptr;
-    int cus = 0;
-    // The two-workgroups-per-CU build has no persistent form: the work loop
-    // pushes it past its 128 registers.
-    uint32_t *q = PAIRED ? nullptr : queue_block(s, &cus);
-    if (q != nullptr) {
-        auto *persistent = attn_fwd_bf16_persistent_kernel<D, RAGGED, false, NQ>;
-        int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)persistent,
-                                                         kThreads, 0) == hipSuccess &&
-            per_cu > 0 && items >= (int64_t)kPersistMinItems * per_cu * cus) {
-            a.queue = q;
-            return tessera_launch(persistent, dim3((unsigned)(per_cu * cus)), dim3(kThreads), s,
-                                  a);
+    if constexpr (!PAIRED) {
+        int cus = 0;
+        uint32_t *q = persistent ? queue_block(s, &cus) : nullptr;
+        if (q != nullptr) {
+            auto *kernel = attn_fwd_bf16_persistent_kernel<D, RAGGED, false, NQ>;
+            int per_cu = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)kernel,
+                                                             kThreads, 0) == hipSuccess &&
+                per_cu > 0 && items > (int64_t)per_cu * cus) {
+                a.queue = q;
+                return tessera_launch(kernel, dim3((unsigned)(per_cu * cus)), dim3(kThreads), s,
+                                      a);
+            }
         }
     }
     return tessera_launch(attn_fwd_bf16_kernel<D, RAGGED, PAIRED, NQ>, dim3((unsigned)items),
                           dim3(kThreads), s, a);
 }
 
-// The bf16 launch shared by both entry points (arguments already validated).
+template <int D>
+int launch_d(const Bf16Args &a, int64_t items, bool ragged, const tessera_attn_tile_config &c,
+             hipStream_t s) {
+    const bool persist = c.persistent != 0;
+    if constexpr (D > 64) {
+        if (ragged) return launch_items<D, true, false, 1>(a, items, persist, s);
+        return launch_items<D, false, false, 1>(a, items, persist, s);
+    } else {
+        if (c.workgroups_per_cu == 2) return launch_items<D, false, true, 1>(a, items, false, s);
+        if (c.query_rows_per_wave == 64) {
+            if (ragged) return launch_items<D, true, false, 2>(a, items, persist, s);
+            return launch_items<D, false, false, 2>(a, items, persist, s);
+        }
+        if (ragged) return launch_items<D, true, false, 1>(a, items, persist, s);
+        return launch_items<D, false, false, 1>(a, items, persist, s);
+    }
+}
+
+// The bf16 launch shared by the entry points (arguments already validated,
+// configuration allowed for these sizes).
 int launch_bf16(const void *q, const void *k, const void *v, void *out, float *lse, int B,
-                int Hq, int Hkv, int Tq, int Tk, int D, int causal, float scale, void *stream) {
+                int Hq, int Hkv, int Tq, int Tk, int D, int causal, float scale,
+                const tessera_attn_tile_config &c, void *stream) {
     Bf16Args a;
     a.q = (const uint16_t *)q;
     a.k = (const uint16_t *)k;
@@ -1075,13 +1136,13 @@ int launch_bf16(const void *q, const void *k, const void *v, void *out, float *l
     a.Tk = Tk;
     a.qoff = Tk - Tq;
     a.G = Hq / Hkv;
-    a.hg = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
+    a.hg = c.heads_per_workgroup;
     a.nqb = kWaves / a.hg;
     a.nslots = a.G / a.hg;
-    const int nq = query_blocks_per_wave(D, causal);
-    a.nqt = (Tq + 32 * nq * a.nqb - 1) / (32 * nq * a.nqb);
-    const int64_t grid = (int64_t)a.nqt * B * Hkv * a.nslots;
-    if (grid > 0x7fffffff) return TESSERA_ERR_TOO_LARGE;
+    const int rows_wg = c.query_rows_per_wave * a.nqb;
+    a.nqt = (Tq + rows_wg - 1) / rows_wg;
+    const int64_t items = (int64_t)a.nqt * B * Hkv * a.nslots;
+    if (items > 0x7fffffff) return TESSERA_ERR_TOO_LARGE;
     a.nbh = B * Hkv;
     a.causal = causal;
     a.qmode = scale < 0.f ? 1 : (scale == 0.f ? 2 : 0);
@@ -1089,25 +1150,9 @@ int launch_bf16(const void *q, const void *k, const void *v, void *out, float *l
 
     hipStream_t s = (hipStream_t)stream;
     const bool ragged = Tk % kKeyTile != 0;
-    // Two workgroups per CU pay off once the grid covers the 512 slots of 256
-    // CUs several times over; on a grid that fills them about once, the pairs
-    // that land together are too uneven in length (causal tiles differ).
-    const bool paired = grid >= kPairedMinGrid && !ragged;
-    if (D == 128) {
-        if (ragged) return launch_items<128, true, false, 1>(a, grid, s);
-        return launch_items<128, false, false, 1>(a, grid, s);
-    } else if (D == 64 && nq == 2) {
-        if (ragged) return launch_items<64, true, false, 2>(a, grid, s);
-        return launch_items<64, false, false, 2>(a, grid, s);
-    } else if (D == 64 && paired) {
-        return launch_items<64, false, true, 1>(a, grid, s);
-    } else if (D == 64) {
-        if (ragged) return launch_items<64, true, false, 1>(a, grid, s);
-        return launch_items<64, false, false, 1>(a, grid, s);
-    } else {
-        if (ragged) return launch_items<32, true, false, 1>(a, grid, s);
-        return launch_items<32, false, false, 1>(a, grid, s);
-    }
+    if (D == 128) return launch_d<128>(a, items, ragged, c, s);
+    if (D == 64) return launch_d<64>(a, items, ragged, c, s);
+    return launch_d<32>(a, items, ragged, c, s);
 }
 
 }  // namespace
@@ -1117,7 +1162,8 @@ extern "C" int tessera_attn_fwd(const void *q, const void *k, const void *v, voi
                                 void *stream) {
     const int st = validate(q, k, v, out, lse, B, Hq, Hkv, T, T, D, causal, scale, 2);
     if (st != TESSERA_OK) return st;
-    return launch_bf16(q, k, v, out, lse, B, Hq, Hkv, T, T, D, causal, scale, stream);
+    return launch_bf16(q, k, v, out, lse, B, Hq, Hkv, T, T, D, causal, scale,
+                       table_config(B, Hq, Hkv, T, T, D, causal), stream);
 }
 
 extern "C" int tessera_attn_fwd_kv(const void *q, const void *k, const void *v, void *out,
@@ -1125,7 +1171,31 @@ extern "C" int tessera_attn_fwd_kv(const void *q, const void *k, const void *v, 
                                    int causal, float scale, void *stream) {
     const int st = validate(q, k, v, out, lse, B, Hq, Hkv, Tq, Tk, D, causal, scale, 2);
     if (st != TESSERA_OK) return st;
-    return launch_bf16(q, k, v, out, lse, B, Hq, Hkv, Tq, Tk, D, causal, scale, stream);
+    return launch_bf16(q, k, v, out, lse, B, Hq, Hkv, Tq, Tk, D, causal, scale,
+                       table_config(B, Hq, Hkv, Tq, Tk, D, causal), stream);
+}
+
+extern "C" int tessera_attn_fwd_with_config(const void *q, const void *k, const void *v,
+                                            void *out, float *lse, int B, int Hq, int Hkv,
+                                            int Tq, int Tk, int D, int causal, float scale,
+                                            const tessera_attn_tile_config *config,
+                                            void *stream) {
+    const int st = validate(q, k, v, out, lse, B, Hq, Hkv, Tq, Tk, D, causal, scale, 2);
+    if (st != TESSERA_OK) return st;
+    if (!config) return TESSERA_ERR_NULL;
+    if (!config_allowed(*config, Hq, Hkv, Tk, D)) return TESSERA_ERR_UNSUPPORTED;
+    return launch_bf16(q, k, v, out, lse, B, Hq, Hkv, Tq, Tk, D, causal, scale, *config, stream);
+}
+
+extern "C" int tessera_attn_fwd_tile_config(int B, int Hq, int Hkv, int Tq, int Tk, int D,
+                                            int causal, tessera_attn_tile_config *config) {
+    if (!config) return TESSERA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || Tk < 1 || Hq % Hkv != 0) return TESSERA_ERR_SHAPE;
+    if (D != 32 && D != 64 && D != 128) return TESSERA_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return TESSERA_ERR_CAUSAL;
+    if (causal == 1 && Tq > Tk) return TESSERA_ERR_SHAPE;
+    *config = table_config(B, Hq, Hkv, Tq, Tk, D, causal);
+    return TESSERA_OK;
 }
 
 extern "C" int tessera_attn_fwd_f32(const float *q, const float *k, const float *v, float *out,

@@ -111,6 +111,55 @@ int tessera_attn_fwd_kv(const void *q, const void *k, const void *v, void *out, 
                         void *stream);
 
 /*
+ * Tile configuration of the bf16 forward (the "autotuned tile sizes" of the
+ * kernel set on the page "Tessera: a from-scratch distillation and serving
+ * stack in one repository", section "The kernel set and its torch
+ * fallback").  A workgroup is eight waves that share each staged 64-key K/V
+ * tile; the configuration sets how its work is cut:
+ *   heads_per_workgroup  1, 2 or 4 query heads of one GQA group per
+ *                        workgroup (must divide Hq / Hkv); the workgroup's
+ *                        query tile then spans 8 / heads_per_workgroup
+ *                        blocks of query_rows_per_wave rows
+ *   query_rows_per_wave  32 or 64 (64: D <= 64 only)
+ *   workgroups_per_cu    1 or 2 (2: D <= 64, 32 rows per wave, and the key
+ *                        count a multiple of 64)
+ *   persistent           0: one workgroup per work item; 1: as many
+ *                        workgroups as the GPU holds at once, taking items
+ *                        from work queues (workgroups_per_cu = 1 only)
+ * Every configuration computes the same result up to rounding.  The library
+ * picks one from a static table built by an offline sweep on MI355X (per
+ * head size, causal or not, and problem size); tessera_attn_fwd and
+ * tessera_attn_fwd_kv use that pick.
+ */
+typedef struct tessera_attn_tile_config {
+    int heads_per_workgroup;
+    int query_rows_per_wave;
+    int workgroups_per_cu;
+    int persistent;
+} tessera_attn_tile_config;
+
+/*
+ * The configuration the library's table picks for these sizes (arguments as
+ * for tessera_attn_fwd_kv; no pointer is read except `config`, which
+ * receives it).  Returns TESSERA_OK, or TESSERA_ERR_NULL / TESSERA_ERR_SHAPE
+ * / TESSERA_ERR_UNSUPPORTED / TESSERA_ERR_CAUSAL for bad arguments.
+ */
+int tessera_attn_fwd_tile_config(int B, int Hq, int Hkv, int Tq, int Tk, int D, int causal,
+                                 tessera_attn_tile_config *config);
+
+/*
+ * tessera_attn_fwd_kv with the tile configuration given explicitly (the
+ * sweep that builds the table times every configuration through this).  A
+ * configuration that these sizes do not allow returns
+ * TESSERA_ERR_UNSUPPORTED before anything is launched; `config` NULL is
+ * TESSERA_ERR_NULL.  Everything else is as for tessera_attn_fwd_kv.
+ */
+int tessera_attn_fwd_with_config(const void *q, const void *k, const void *v, void *out,
+                                 float *lse, int B, int Hq, int Hkv, int Tq, int Tk, int D,
+                                 int causal, float scale, const tessera_attn_tile_config *config,
+                                 void *stream);
+
+/*
  * fp32 attention forward: the same operation and arguments with float32
  * q, k, v and out, computed in fp32 throughout.
  */

@@ -234,3 +234,40 @@ def test_paged_noalloc_bad_arguments_are_rejected_before_launch(kwargs, code):
     # every check, the scratch limit included, comes before any HIP call
     assert call_paged_noalloc(**kwargs) == code
     assert "scratch" in binding.status_string(binding.ERR_SCRATCH)
+
+
+def test_tile_table_is_the_sweeps_winners():
+    """The table compiled into the library (csrc/tile_table.inc) holds exactly
+    the winners that the committed sweep (profiles/tile_sweep_attn_fwd_bf16.md)
+    recorded, and each winner is the fastest configuration of its section."""
+    import re
+
+    from attention_flashattention_fwd_amd import autotune
+    table = autotune.parse_table(
+        (ROOT / "attention_flashattention_fwd_amd" / "csrc" / "tile_table.inc").read_text())
+    report = (ROOT / "profiles" / "tile_sweep_attn_fwd_bf16.md").read_text()
+    recorded = sorted(tuple(int(x) for x in m.group(1).split(","))
+                      for m in re.finditer(r"^\s+rule: ([\d, ]+)$", report, re.M))
+    assert table == recorded and len(table) == 12
+    for sec in re.split(r"^## ", report, flags=re.M)[1:]:
+        m = re.match(r"D=(\d+), causal=(\d), (large|small)", sec)
+        if not m:
+            continue
+        timings = [(float(t), tuple(int(x) for x in c.split(",")), "winner" in w)
+                   for c, w, t in re.findall(r"^\| \(([\d, ]+)\)( \*\*winner\*\*)? \| ([\d.]+) \|",
+                                             sec, re.M)]
+        best = min(timings)
+        assert best[2], sec.splitlines()[0]
+        key = (int(m.group(1)), int(m.group(2)), int(m.group(3) == "large"))
+        assert key + best[1] in table
+
+
+def test_table_picks_fit_the_sizes():
+    # the pick for a GQA group of 3 falls back to one head per workgroup, and a
+    # ragged key count to one workgroup per CU
+    c = binding.tile_config(2, 6, 2, 200, 200, 64, 1)
+    assert c.heads_per_workgroup == 1
+    c = binding.tile_config(16, 16, 4, 4095, 4095, 64, 1)
+    assert c.workgroups_per_cu == 1
+    with pytest.raises(RuntimeError):
+        binding.tile_config(1, 4, 2, 10, 10, 96, 1)

@@ -187,6 +187,60 @@ def test_persistent_launches_on_two_streams():
         assert torch.equal(o2, want2[0]) and torch.equal(l2, want2[1])
 
 
+# Every tile configuration the table may pick from (tessera_attn_fwd_with_config),
+# for each head size, causal or not, with T ragged and a multiple of the key
+# tile: 1056 work items at four heads per workgroup, so the persistent ones do
+# run persistently.  Sampled rows of each output against the oracle.
+_CONFIG_INPUTS = {}
+
+
+def _config_case(D, T):
+    if (D, T) not in _CONFIG_INPUTS:
+        q, k, v = inputs.make_qkv(8, 16, 4, T, D, "bf16", seed=D + T)
+        rows = np.unique(np.random.default_rng(D + T).integers(0, 8 * 16 * T, 160)).astype(np.int64)
+        bits = [inputs.bits(t) for t in (q, k, v)]
+        refs = {c: oracle.attn_rows(*bits, c, inputs.default_scale(D), rows) for c in (True, False)}
+        _CONFIG_INPUTS[(D, T)] = ([t.cuda() for t in (q, k, v)], rows, refs)
+    return _CONFIG_INPUTS[(D, T)]
+
+
+def _all_configs(D, T):
+    from attention_flashattention_fwd_amd import autotune
+    return autotune.configs(4, T, D)
+
+
+@pytest.mark.parametrize("D,T,causal,cfg", [
+    (D, T, causal, cfg) for D in (128, 64, 32) for T in (2112, 2100) for causal in (True, False)
+    for cfg in _all_configs(D, T)])
+def test_every_tile_configuration(D, T, causal, cfg):
+    (q, k, v), rows, refs = _config_case(D, T)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    binding.attn_fwd_with_config_into(q, k, v, out, lse, binding.TileConfig(*cfg), causal)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).to(q.device)
+    o = out.reshape(-1, D)[idx].float().cpu().numpy().astype(np.float64)
+    l = lse.reshape(-1)[idx].cpu().numpy().astype(np.float64)
+    check_close(o, l, *refs[causal], "bf16", f"D={D} T={T} causal={causal} config={cfg}")
+
+
+def test_tile_configurations_the_sizes_do_not_allow():
+    q, k, v = (t.cuda() for t in inputs.make_qkv(1, 12, 4, 100, 128, "bf16", seed=1))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    for cfg in [(2, 32, 1, 0),    # 2 does not divide the group of 3
+                (1, 64, 1, 0),    # 64 rows per wave at D = 128
+                (1, 32, 2, 0),    # two workgroups per CU at D = 128
+                (3, 32, 1, 0), (1, 48, 1, 0), (1, 32, 3, 0), (1, 32, 1, 2)]:
+        with pytest.raises(RuntimeError, match="unsupported"):
+            binding.attn_fwd_with_config_into(q, k, v, out, lse, binding.TileConfig(*cfg))
+    q64, k64, v64 = (t.cuda() for t in inputs.make_qkv(1, 4, 4, 100, 64, "bf16", seed=1))
+    with pytest.raises(RuntimeError, match="unsupported"):   # ragged T, two per CU
+        binding.attn_fwd_with_config_into(q64, k64, v64, torch.empty_like(q64),
+                                          torch.empty(q64.shape[:3], device=q64.device),
+                                          binding.TileConfig(1, 32, 2, 0))
+
+
 # (D, rate, seed, B, Hq, Hkv, T, causal): the last two run the two-workgroups-
 # per-CU build (2048 workgroups) and the two-query-blocks-per-wave build.
 GROWING = [
