@@ -271,3 +271,12 @@ def test_table_picks_fit_the_sizes():
     assert c.workgroups_per_cu == 1
     with pytest.raises(RuntimeError):
         binding.tile_config(1, 4, 2, 10, 10, 96, 1)
+
+
+def test_phase_probe_instruments_the_current_kernel_source():
+    """Every anchor of the per-phase timing tool is found once in the kernel
+    source, so the instrumented build follows the kernel as it changes."""
+    from attention_flashattention_fwd_amd import phase_probe
+    text = phase_probe.instrumented_source(phase_probe.SOURCE.read_text())
+    assert text.count("__builtin_amdgcn_s_memtime") == 4
+    assert "tessera_probe_set" in text
