@@ -112,7 +112,8 @@ struct Bf16Args {
 // line per counter); the last workgroup to finish sets them back to zero for
 // the next launch.  A persistent launch pays an atomic round trip per item and
 // its workgroups cannot overlap one item's end with the next one's start, so
-// it is used only where each slot gets several items (kPersistMinItems).
+// it is used only where the tile table's sweep found it faster, and only when
+// there are more items than workgroup slots.
 constexpr int kQueues = 8;
 constexpr int kTicket = kQueues;                       // counter of items handed out
 constexpr int kDone = kQueues + 1;                     // counter of finished workgroups
@@ -1029,7 +1030,6 @@ bool config_allowed(const tessera_attn_tile_config &c, int Hq, int Hkv, int Tk, 
 // ---------------------------------------------------------------------------
 constexpr int kQueueSlots = 64;
 constexpr int kMaxDevices = 64;
-constexpr int kPersistMinItems = 4;   // items per workgroup slot for a persistent launch
 
 }  // namespace
 
