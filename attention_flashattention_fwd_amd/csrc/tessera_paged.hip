@@ -429,10 +429,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Merges the splits of every query row whose sequence has more than one:
-// one wave per row, four rows per workgroup.
+// one wave per row, four rows per workgroup.  Lane s first takes split s's
+// log2-sum-exp (64 splits at a time), so the weights cost one load per lane;
+// the partial rows are then read eight splits at a time, all eight loads in
+// flight together.  The sums run over the splits in order, as in the formula.
 template <int D>
 __global__ void __launch_bounds__(256) paged_combine_kernel(PagedArgs a, int64_t rows) {
-    constexpr int kPer = (D + 63) / 64;
+    constexpr int kPer = D / 64 > 0 ? D / 64 : 1;   // dims per lane
+    constexpr int kUnroll = 8;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
@@ -452,30 +456,60 @@ __global__ void __launch_bounds__(256) paged_combine_kernel(PagedArgs a, int64_t
     uint16_t *dst = a.o + row * D;
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {
 #pragma unroll
-        for (int k = 0; k < kPer; ++k)
+        for (int k = 0; k < (D + 63) / 64; ++k)
             if (lane + 64 * k < D) dst[lane + 64 * k] = kBadBf16;
         if (lane == 0) a.lse[row] = __uint_as_float(kBadBits);
         return;
     }
     mx = wave_max(mx);
     const float m_use = mx == -INFINITY ? 0.f : mx;
+    // Lane d0 = kPer * lane holds dims d0 .. d0 + kPer - 1 (at D=32 the upper
+    // half of the wave reads dims of its own row again and stores nothing).
+    const int d0 = (kPer * lane) % D;
+    const float *src0 = a.ws_o + row * a.nsplit * D + d0;
     float o[kPer] = {};
     float wsum = 0.f;
-    for (int s = 0; s < nsb; ++s) {
-        const float w = __builtin_amdgcn_exp2f(pl[s] - m_use);
-        wsum += w;
-        const float *src = a.ws_o + (row * a.nsplit + s) * D;
+    for (int c0 = 0; c0 < nsb; c0 += 64) {
+        const int cnt = min(64, nsb - c0);
+        const float wl = lane < cnt ? __builtin_amdgcn_exp2f(pl[c0 + lane] - m_use) : 0.f;
+        int j = 0;
+        for (; j + kUnroll <= cnt; j += kUnroll) {
+            float x[kUnroll][kPer];
 #pragma unroll
-        for (int k = 0; k < kPer; ++k)
-            if (lane + 64 * k < D) o[k] = __builtin_fmaf(w, src[lane + 64 * k], o[k]);
+            for (int u = 0; u < kUnroll; ++u) {
+                const float *p = src0 + (int64_t)(c0 + j + u) * D;
+                if constexpr (kPer == 2) {
+                    const f32x2 v = *(const f32x2 *)p;
+                    x[u][0] = v[0];
+                    x[u][1] = v[1];
+                } else {
+                    x[u][0] = *p;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const float w = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), j + u));
+                wsum += w;
+#pragma unroll
+                for (int k = 0; k < kPer; ++k) o[k] = __builtin_fmaf(w, x[u][k], o[k]);
+            }
+        }
+        for (; j < cnt; ++j) {
+            const float *p = src0 + (int64_t)(c0 + j) * D;
+            const float w = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), j));
+            wsum += w;
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) o[k] = __builtin_fmaf(w, p[k], o[k]);
+        }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    if (kPer * lane < D) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k)
-        if (lane + 64 * k < D) {
+        for (int k = 0; k < kPer; ++k) {
             const __bf16 y = (__bf16)(o[k] * inv);
-            dst[lane + 64 * k] = __builtin_bit_cast(uint16_t, y);
+            dst[d0 + k] = __builtin_bit_cast(uint16_t, y);
         }
+    }
     if (lane == 0) a.lse[row] = wsum > 0.f ? (mx + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
