@@ -14,6 +14,9 @@
 // its pieces of w in registers across all the rows it handles, so w is read
 // once per wave.  Rows of more than 8192 values take a second kernel that
 // reads the row twice (the second time mostly from L2) instead of holding it.
+// y is stored non-temporally: the stores then stay out of the way of the
+// loads in the caches, measured 2-27% faster with the caches cold (inputs
+// larger than the 256 MB Infinity Cache) and no slower with them warm.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -99,7 +102,7 @@ rmsnorm_reg_kernel(const u32x4 *x, const u32x4 *__restrict__ w,
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             const int c = lane + 64 * i;
-            if (c < nvec) yr[c] = scaled(v[i], g[i], rstd);
+            if (c < nvec) __builtin_nontemporal_store(scaled(v[i], g[i], rstd), &yr[c]);
         }
     }
 }
@@ -117,7 +120,8 @@ rmsnorm_stream_kernel(const u32x4 *x, const u32x4 *__restrict__ w,
         for (int c = lane; c < nvec; c += 64) s += squares(xr[c]);
         const float rstd = 1.f / sqrtf(wave_sum(s) * inv_n + eps);
         u32x4 *yr = y + r * nvec;
-        for (int c = lane; c < nvec; c += 64) yr[c] = scaled(xr[c], w[c], rstd);
+        for (int c = lane; c < nvec; c += 64)
+            __builtin_nontemporal_store(scaled(xr[c], w[c], rstd), &yr[c]);
     }
 }
 
