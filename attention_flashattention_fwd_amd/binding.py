@@ -442,7 +442,7 @@ def paged_decode_into(q, k_cache, v_cache, block_table, context_lens, out, lse, 
                       causal: bool = True, scale: float | None = None, stream=None) -> None:
     """Decode attention over a block-paged cache into preallocated out
     [B,Hq,Tq,D] bfloat16 and lse [B,Hq,Tq] float32; `workspace` is a uint8
-    tensor of at least paged_workspace_bytes(...) bytes (or None when that is 0)."""
+    tensor of at least paged_workspace_bytes(...) bytes."""
     import torch
 
     B, Hq, Hkv, Tq, D, nblk, bs, maxb = _check_paged(q, k_cache, v_cache, block_table,

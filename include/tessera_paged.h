@@ -41,15 +41,17 @@
  * Bad device data.  The lengths and the table live in device memory, so they
  * cannot be checked before the launch.  A length outside
  * [0, max_blocks * block_size], or a table entry in use outside
- * [0, num_blocks), is not followed: no cache memory is read through it, and
- * every out and lse value of that sequence becomes NaN.
+ * [0, num_blocks), is not followed: no memory outside the caches is read
+ * through it, and every out and lse value of that sequence becomes NaN.
  *
- * Workspace.  Long sequences are split into several parts that run in
- * parallel; their partial results are merged through their lse.  The
+ * Workspace.  The 32-key tiles of each KV head, over all sequences, are
+ * shared out in equal contiguous parts among a fixed set of waves (1536 in
+ * all, fewer for small calls), so a sequence may be cut into pieces held by
+ * several waves; their partial results are merged through their lse.  The
  * caller passes a device workspace of at least
- * tessera_paged_decode_workspace(...) bytes, 16-byte aligned (NULL with 0
- * bytes when that returns 0).  Its contents on entry do not matter; two calls
- * must not use one workspace at the same time.
+ * tessera_paged_decode_workspace(...) bytes (always more than 0), 16-byte
+ * aligned.  Its contents on entry do not matter; two calls must not use one
+ * workspace at the same time.
  *
  * Ownership, streams and errors: as in tessera_attn.h (scale any finite
  * float, causal 0 or 1; no output may overlap an input, the workspace or the
@@ -65,9 +67,9 @@
 extern "C" {
 #endif
 
-/* Bytes of workspace tessera_paged_decode needs for these sizes: 0 when none
- * is needed, or -status (a negative tessera_attn_status) when the sizes are
- * invalid or unsupported. */
+/* Bytes of workspace tessera_paged_decode needs for these sizes (more than
+ * 0), or -status (a negative tessera_attn_status) when the sizes are invalid
+ * or unsupported. */
 long long tessera_paged_decode_workspace(int B, int Hq, int Hkv, int Tq, int D, int block_size,
                                          int max_blocks);
 
@@ -81,7 +83,7 @@ int tessera_paged_decode(const void *q, const void *k_cache, const void *v_cache
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * decode as tessera_paged_decode, with the same arguments except the
- * workspace, and identical results.  The split partials go to a fixed
+ * workspace, and identical results.  The partial results go to a fixed
  * scratch buffer of tessera_paged_decode_scratch_limit() bytes (32 MiB) that
  * the library holds in each GPU's memory from its first use on that GPU until
  * the process ends; the call itself allocates nothing.  Sizes whose workspace

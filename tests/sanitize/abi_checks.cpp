@@ -105,7 +105,8 @@ int main() {
     expect("paged bs", tessera_paged_decode_noalloc(q, k, v, bt, cl, o, l, 2, 8, 2, 2, 64, 64, 8,
                                                     100, 1, 0.125f, nullptr),
            TESSERA_ERR_UNSUPPORTED);
-    expect("paged scratch", tessera_paged_decode_noalloc(q, k, v, bt, cl, o, l, 64, 32, 8, 1, 128,
+    // 32 query rows per KV head in 8 x 256 slots: 34 MB of workspace > 32 MiB
+    expect("paged scratch", tessera_paged_decode_noalloc(q, k, v, bt, cl, o, l, 64, 256, 8, 1, 128,
                                                          64, 16, 4096, 1, 0.125f, nullptr),
            TESSERA_ERR_SCRATCH);
     expect("paged sizes", tessera_paged_decode_workspace(64, 32, 8, 1, 128, 16, 1024) > 0, 1);

@@ -151,17 +151,27 @@ def test_bwd_bad_arguments_are_rejected_before_launch(kwargs, code):
     assert call_bwd(**kwargs) == code
 
 
+def paged_layout_bytes(B, Hq, Hkv, Tq, D, block_size, max_blocks):
+    """The workspace layout written out: per KV head, one slot per decode wave
+    (1536 waves in all, no more than the tiles a head can have) plus one per
+    sequence; an fp32 log2-sum-exp and an fp32 row of D per query row of the
+    head in each slot; two ints per (sequence, KV head)."""
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    wg = max(1, min(1536 // Hkv, B * ((max_blocks * block_size + 31) // 32)))
+    cells = Hkv * (wg + B) * (Hq // Hkv) * Tq
+    return r256(cells * 4) + cells * D * 4 + r256(B * Hkv * 8)
+
+
 def test_paged_workspace_sizes():
-    # the serving batch: 64 x 8 (sequence, KV head) pairs of up to 16384 tokens
-    # -> splits of 1024 keys (64 blocks of 16, the most one split may span),
-    # 16 per sequence; 2048 query rows
-    cells = 64 * 32 * 1 * 16
-    assert binding.raw_paged_workspace(64, 32, 8, 1, 128, 16, 1024) == cells * 4 + cells * 128 * 4
-    # short sequences fit one split: no workspace
-    assert binding.raw_paged_workspace(2, 4, 2, 1, 64, 16, 8) == 0
-    # 1600 tokens in splits of 256: 7 per sequence; the lse part rounds up to 256 bytes
-    cells = 1 * 8 * 2 * 7
-    assert binding.raw_paged_workspace(1, 8, 2, 2, 32, 16, 100) == 512 + cells * 32 * 4
+    # the serving batch: 192 waves per KV head, 256 slots, 4 query rows each
+    assert binding.raw_paged_workspace(64, 32, 8, 1, 128, 16, 1024) == 32768 + 4194304 + 4096
+    # short sequences: at most 8 tiles per head -> 8 waves, 10 slots
+    assert binding.raw_paged_workspace(2, 4, 2, 1, 64, 16, 8) == 256 + 10240 + 256
+    # 1600 tokens: 50 tiles -> 50 waves, 51 slots of 8 rows; the lse part rounds up
+    assert binding.raw_paged_workspace(1, 8, 2, 2, 32, 16, 100) == 3328 + 104448 + 256
+    for shape in [(64, 32, 8, 1, 128, 16, 1024), (2, 4, 2, 1, 64, 16, 8), (1, 8, 2, 2, 32, 16, 100),
+                  (3, 8, 1, 4, 64, 32, 7), (1, 64, 64, 1, 128, 16, 4096)]:
+        assert binding.raw_paged_workspace(*shape) == paged_layout_bytes(*shape), shape
     assert binding.raw_paged_workspace(1, 8, 2, 9, 32, 16, 100) == -binding.ERR_UNSUPPORTED
     assert binding.raw_paged_workspace(1, 8, 2, 1, 32, 24, 100) == -binding.ERR_UNSUPPORTED
     assert binding.raw_paged_workspace(1, 8, 3, 1, 32, 16, 100) == -binding.ERR_SHAPE
@@ -227,8 +237,8 @@ def test_paged_noalloc_scratch_limit():
     (dict(scale=float("inf")), binding.ERR_SCALE),
     (dict(kc=KC + 8), binding.ERR_ALIGN),
     (dict(o=KC + 4096), binding.ERR_ALIAS),
-    # partials of 64 x 32 query rows over 64 splits: 68 MB of workspace > 32 MiB
-    (dict(B=64, Hq=32, Hkv=8, Tq=1, D=128, max_blocks=4096), binding.ERR_SCRATCH),
+    # 32 query rows per KV head in 8 x 256 slots: 34 MB of workspace > 32 MiB
+    (dict(B=64, Hq=256, Hkv=8, Tq=1, D=128, max_blocks=4096), binding.ERR_SCRATCH),
 ])
 def test_paged_noalloc_bad_arguments_are_rejected_before_launch(kwargs, code):
     # every check, the scratch limit included, comes before any HIP call

@@ -68,11 +68,12 @@ def test_noalloc_matches_the_workspace_entry_on_two_calls():
 
 
 def test_noalloc_rejects_what_exceeds_the_scratch():
-    q = torch.zeros(64, 32, 1, 128, dtype=torch.bfloat16, device=DEV)
+    # 32 query rows per KV head: 8 x 256 slots of 32 rows, 34 MB of workspace
+    q = torch.zeros(64, 256, 1, 128, dtype=torch.bfloat16, device=DEV)
     kc = torch.zeros(8, 8, 16, 128, dtype=torch.bfloat16, device=DEV)
     table = torch.zeros(64, 4096, dtype=torch.int32, device=DEV)
     lens = torch.zeros(64, dtype=torch.int32, device=DEV)
-    out, lse = torch.empty_like(q), torch.empty(64, 32, 1, device=DEV)
-    assert binding.paged_workspace_bytes(64, 32, 8, 1, 128, 16, 4096) > binding.paged_scratch_limit()
+    out, lse = torch.empty_like(q), torch.empty(64, 256, 1, device=DEV)
+    assert binding.paged_workspace_bytes(64, 256, 8, 1, 128, 16, 4096) > binding.paged_scratch_limit()
     with pytest.raises(RuntimeError, match="scratch"):
         binding.paged_decode_noalloc_into(q, kc, kc, table, lens, out, lse)
