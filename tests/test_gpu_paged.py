@@ -47,9 +47,18 @@ def check_paged(o, l, O_ref, l_ref, what=""):
     assert el.max() <= BF16_MAX and el.mean() <= BF16_MEAN, stats
 
 
-# (B, Hq, Hkv, Tq, D, block_size, lengths, causal).  The lengths cross block,
-# tile (32 keys) and split boundaries (splits of 256 keys at these sizes) and
-# include empty sequences and sequences shorter than Tq.
+# (B, Hq, Hkv, Tq, D, block_size, lengths, causal).  The lengths cross block
+# and tile (32 keys) boundaries and the boundaries of the waves' shares (at
+# these sizes most waves hold one tile, so a long sequence is cut into many
+# pieces: 94 for the 3000-token one, more than the merge's 64 at a time), and
+# include empty sequences and sequences shorter than Tq.  More than 64
+# sequences give each lane several sequences to count; a single long
+# sequence is cut among all waves of its head.
+_rng = np.random.default_rng(5)
+MANY_100 = [int(x) for x in _rng.integers(0, 600, size=100)]
+MANY_100[7] = MANY_100[64] = MANY_100[99] = 0
+MANY_300 = [int(x) for x in _rng.integers(0, 200, size=300)]
+MANY_300[0] = MANY_300[150] = 0
 CASES = [
     (9, 8, 2, 1, 128, 16, [1, 15, 16, 17, 100, 511, 512, 513, 3000], True),
     (6, 16, 4, 4, 64, 32, [0, 2, 4, 33, 1000, 2047], True),
@@ -58,6 +67,9 @@ CASES = [
     (4, 4, 1, 3, 64, 64, [0, 1, 5, 4100], True),         # MQA, a 17-split sequence
     (4, 8, 8, 1, 128, 16, [7, 300, 301, 900], False),
     (3, 8, 2, 8, 64, 16, [5, 64, 700], False),           # non-causal, n < Tq included
+    (100, 8, 2, 1, 64, 16, MANY_100, True),               # two sequences per lane
+    (300, 4, 1, 2, 32, 16, MANY_300, True),               # five per lane, MQA
+    (1, 32, 8, 1, 128, 16, [16000], True),                # one sequence, 192 pieces per head
 ]
 
 
