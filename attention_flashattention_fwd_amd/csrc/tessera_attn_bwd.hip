@@ -431,15 +431,23 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 
     TileStager<D, kKvThreads> qs_, ds_;
     float l_in = 0.f, m_in = 0.f;
-    auto fetch = [&](int step) __attribute__((always_inline)) {
-        const int g = step / per_head, q0 = (qt_first + step % per_head) * kTileRows;
-        const int64_t hrow = (head0 + g) * T;
+    // Steps are fetched in order; the (head, query tile) of the next fetch is
+    // kept as two counters (a division by per_head would cost tens of
+    // instructions per step).
+    int f_g = 0, f_qi = 0;
+    auto fetch = [&]() __attribute__((always_inline)) {
+        const int q0 = (qt_first + f_qi) * kTileRows;
+        const int64_t hrow = (head0 + f_g) * T;
         qs_.fetch(a.q + hrow * D, q0, T, tid);
         ds_.fetch(a.dout + hrow * D, q0, T, tid);
         if (tid < kTileRows) {
             const bool ok = q0 + tid < T;
             l_in = ok ? a.lse[hrow + q0 + tid] * kLog2e : INFINITY;   // P = 0 past T
             m_in = ok ? a.delta[hrow + q0 + tid] : 0.f;
+        }
+        if (++f_qi == per_head) {
+            f_qi = 0;
+            ++f_g;
         }
     };
     auto store = [&](int buf) __attribute__((always_inline)) {
@@ -451,13 +459,15 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
         }
     };
 
-    fetch(0);
+    fetch();
     store(0);
     __syncthreads();
+    int c_qi = 0;   // query tile of the current step, counted like f_qi
     for (int step = 0; step < nsteps; ++step) {
         const int cur = step & 1;
-        if (step + 1 < nsteps) fetch(step + 1);
-        const int q0 = (qt_first + step % per_head) * kTileRows;
+        if (step + 1 < nsteps) fetch();
+        const int q0 = (qt_first + c_qi) * kTileRows;
+        if (++c_qi == per_head) c_qi = 0;
         const LDS_AS char *qt = (const LDS_AS char *)lds_q[cur];
         const LDS_AS char *dt = (const LDS_AS char *)lds_d[cur];
         const bool need_mask = causal && q0 < kw0 + 31;
@@ -472,17 +482,27 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
             for (int ks = 0; ks < D / 16; ++ks) sp = mfma32(read_row<D>(lhs, off, h, ks), kv[ks], sp);
             f32x4 (&xp)[4][64] = lds_p[h][w & 3];
             if (!dk_wave) {
+                // exponent of P; on a step that crosses the diagonal, query
+                // rows before this lane's key get -inf (one branch per step, so
+                // the other steps run no mask instructions)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = 32 * h + 8 * j + 4 * hi;
-                    const f32x4 l4 = *(const LDS_AS f32x4 *)&lds_l[cur][r];
+                    const f32x4 l4 = *(const LDS_AS f32x4 *)&lds_l[cur][32 * h + 8 * j + 4 * hi];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int i = 4 * j + u;
-                        float xe = __builtin_fmaf(sp[i], c, -l4[u]);
-                        if (need_mask && q0 + r + u < key) xe = -INFINITY;
-                        sp[i] = __builtin_amdgcn_exp2f(xe);
-                    }
+                    for (int u = 0; u < 4; ++u)
+                        sp[4 * j + u] = __builtin_fmaf(sp[4 * j + u], c, -l4[u]);
+                }
+                if (need_mask) {
+                    const int first = key - q0 - 32 * h - 4 * hi;   // first visible register row
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (8 * (i >> 2) + (i & 3) < first) sp[i] = -INFINITY;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        sp[4 * j + u] = __builtin_amdgcn_exp2f(sp[4 * j + u]);
                     *(LDS_AS f32x4 *)&xp[j][lane] =
                         f32x4{sp[4 * j], sp[4 * j + 1], sp[4 * j + 2], sp[4 * j + 3]};
                 }
@@ -571,15 +591,22 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
 
     TileStager<D, kKvThreads> qs_, ds_;
     float l_in = 0.f, m_in = 0.f;
-    auto fetch = [&](int step) __attribute__((always_inline)) {
-        const int g = step / per_head, q0 = (qt_first + step % per_head) * kTileRows;
-        const int64_t hrow = (head0 + g) * T;
+    // Steps are fetched in order (in either role's loop); the (head, query
+    // tile) of the next fetch is kept as two counters, not divided out.
+    int f_g = 0, f_qi = 0;
+    auto fetch = [&]() __attribute__((always_inline)) {
+        const int q0 = (qt_first + f_qi) * kTileRows;
+        const int64_t hrow = (head0 + f_g) * T;
         qs_.fetch(a.q + hrow * D, q0, T, tid);
         ds_.fetch(a.dout + hrow * D, q0, T, tid);
         if (tid < kTileRows) {
             const bool ok = q0 + tid < T;
             l_in = ok ? a.lse[hrow + q0 + tid] * kLog2e : INFINITY;   // P = 0 past T
             m_in = ok ? a.delta[hrow + q0 + tid] : 0.f;
+        }
+        if (++f_qi == per_head) {
+            f_qi = 0;
+            ++f_g;
         }
     };
     auto store = [&](int step) __attribute__((always_inline)) {
@@ -591,9 +618,8 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
             lds_m[b3][tid] = m_in;
         }
     };
-    auto q0_of = [&](int step) { return (qt_first + step % per_head) * kTileRows; };
 
-    fetch(0);
+    fetch();
     store(0);
     __syncthreads();
     // Each role runs its own loop (registers are allocated per role); both
@@ -603,10 +629,12 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
         __syncthreads();
     };
     if (!dk_wave) {
+        int c_qi = 0;   // query tile of the current step, counted like f_qi
         for (int step = 0; step <= nsteps; ++step) {
-            if (step + 1 < nsteps) fetch(step + 1);
+            if (step + 1 < nsteps) fetch();
             if (step < nsteps) {
-                const int q0 = q0_of(step);
+                const int q0 = (qt_first + c_qi) * kTileRows;
+                if (++c_qi == per_head) c_qi = 0;
                 const bool need_mask = causal && q0 < kw0 + 31;
                 const LDS_AS char *qt = (const LDS_AS char *)lds_q[step % 3];
                 const LDS_AS char *dt = (const LDS_AS char *)lds_d[step & 1];
@@ -618,17 +646,26 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
                     for (int ks = 0; ks < D / 16; ++ks)
                         sp = mfma32(read_row<D>(qt, off, h, ks), kv[ks], sp);
                     f32x4 (&xp)[4][64] = lds_p[step & 1][h][w & 3];
+                    // exponent of P, masked in one branch per step (as above)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int r = 32 * h + 8 * j + 4 * hi;
-                        const f32x4 l4 = *(const LDS_AS f32x4 *)&lds_l[step % 3][r];
+                        const f32x4 l4 =
+                            *(const LDS_AS f32x4 *)&lds_l[step % 3][32 * h + 8 * j + 4 * hi];
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int i = 4 * j + u;
-                            float xe = __builtin_fmaf(sp[i], c, -l4[u]);
-                            if (need_mask && q0 + r + u < key) xe = -INFINITY;
-                            sp[i] = __builtin_amdgcn_exp2f(xe);
-                        }
+                        for (int u = 0; u < 4; ++u)
+                            sp[4 * j + u] = __builtin_fmaf(sp[4 * j + u], c, -l4[u]);
+                    }
+                    if (need_mask) {
+                        const int first = key - q0 - 32 * h - 4 * hi;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            if (8 * (i >> 2) + (i & 3) < first) sp[i] = -INFINITY;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            sp[4 * j + u] = __builtin_amdgcn_exp2f(sp[4 * j + u]);
                         *(LDS_AS f32x4 *)&xp[j][lane] =
                             f32x4{sp[4 * j], sp[4 * j + 1], sp[4 * j + 2], sp[4 * j + 3]};
                     }
@@ -648,7 +685,7 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
     } else {
         f32x16 dp[2];   // dP of the step before (both halves)
         for (int step = 0; step <= nsteps; ++step) {
-            if (step + 1 < nsteps) fetch(step + 1);
+            if (step + 1 < nsteps) fetch();
             if (step > 0) {
                 // dS and dk of the step before: its Q tile, Delta and P are still in LDS
                 const int prev = step - 1;
