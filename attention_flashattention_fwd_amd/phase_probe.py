@@ -11,7 +11,10 @@ then runs it on forward workloads and reports, from the GPU's own clocks:
     MFMA phases and of its vector (softmax) phases, separately for the
     leading and the lagging wave of each SIMD;
   * per XCD: the last end, the earliest CU end and microseconds per tile, which
-    show how evenly the dies share the work.
+    show how evenly the dies share the work;
+  * a least-squares fit of item duration = fixed part + tiles x per-tile part
+    (the fixed part is what an item's start and end cost), and the spread of
+    the items' starts and ends over the launch.
 
 The instrumentation adds only timestamp reads and one store per wave at the
 start and end of each item; the timed launch rate of the instrumented build
@@ -149,6 +152,17 @@ def analyse(rec: np.ndarray, items: int) -> dict:
                         "last_end_us": max(ends), "first_cu_end_us": min(ends),
                         "us_per_tile": float(np.median(dur / np.maximum(tiles[s], 1)))})
     out["per_xcd"] = per_xcd
+    # item duration = fixed part + per-tile part (least squares over the items):
+    # the fixed part is an item's start (Q, the first K/V tiles) and end
+    dur_us = (end - start) / 100.0
+    fit = np.linalg.lstsq(np.vstack([np.ones(len(tiles)), tiles]).T.astype(float), dur_us,
+                          rcond=None)[0]
+    out["item_fixed_us"] = float(fit[0])
+    out["item_us_per_tile"] = float(fit[1])
+    out["start_us_quantiles"] = [float(np.percentile((start - t0) / 100.0, q))
+                                 for q in (10, 50, 90, 100)]
+    out["end_us_quantiles"] = [float(np.percentile((end - t0) / 100.0, q))
+                               for q in (10, 50, 90, 100)]
     return out
 
 
