@@ -46,7 +46,7 @@
  *
  * Workspace.  The 32-key tiles of each KV head, over all sequences, are
  * shared out in equal contiguous parts among a fixed set of waves (1536 in
- * all, fewer for small calls), so a sequence may be cut into pieces held by
+ * all, 2048 at D = 32, fewer for small calls), so a sequence may be cut into pieces held by
  * several waves; their partial results are merged through their lse.  The
  * caller passes a device workspace of at least
  * tessera_paged_decode_workspace(...) bytes (always more than 0), 16-byte

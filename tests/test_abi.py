@@ -153,11 +153,12 @@ def test_bwd_bad_arguments_are_rejected_before_launch(kwargs, code):
 
 def paged_layout_bytes(B, Hq, Hkv, Tq, D, block_size, max_blocks):
     """The workspace layout written out: per KV head, one slot per decode wave
-    (1536 waves in all, no more than the tiles a head can have) plus one per
+    (1536 waves in all, 2048 at D=32, no more than the tiles a head can have) plus one per
     sequence; an fp32 log2-sum-exp and an fp32 row of D per query row of the
     head in each slot; two ints per (sequence, KV head)."""
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    wg = max(1, min(1536 // Hkv, B * ((max_blocks * block_size + 31) // 32)))
+    waves = 2048 if D == 32 else 1536
+    wg = max(1, min(waves // Hkv, B * ((max_blocks * block_size + 31) // 32)))
     cells = Hkv * (wg + B) * (Hq // Hkv) * Tq
     return r256(cells * 4) + cells * D * 4 + r256(B * Hkv * 8)
 
@@ -170,7 +171,8 @@ def test_paged_workspace_sizes():
     # 1600 tokens: 50 tiles -> 50 waves, 51 slots of 8 rows; the lse part rounds up
     assert binding.raw_paged_workspace(1, 8, 2, 2, 32, 16, 100) == 3328 + 104448 + 256
     for shape in [(64, 32, 8, 1, 128, 16, 1024), (2, 4, 2, 1, 64, 16, 8), (1, 8, 2, 2, 32, 16, 100),
-                  (3, 8, 1, 4, 64, 32, 7), (1, 64, 64, 1, 128, 16, 4096)]:
+                  (3, 8, 1, 4, 64, 32, 7), (1, 64, 64, 1, 128, 16, 4096),
+                  (64, 32, 8, 1, 32, 16, 1024), (2, 8, 1, 1, 32, 16, 4096)]:
         assert binding.raw_paged_workspace(*shape) == paged_layout_bytes(*shape), shape
     assert binding.raw_paged_workspace(1, 8, 2, 9, 32, 16, 100) == -binding.ERR_UNSUPPORTED
     assert binding.raw_paged_workspace(1, 8, 2, 1, 32, 24, 100) == -binding.ERR_UNSUPPORTED
