@@ -117,7 +117,8 @@ def check_rows(torch, out, lse, D, ref):
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__,
                                 formatter_class=argparse.RawDescriptionHelpFormatter)
-    p.add_argument("--out", default=str(ROOT / "gpurun_out" / "tune"))
+    p.add_argument("--out", default="tile_sweep_out",
+                   help="folder for the table and the report (default: ./tile_sweep_out)")
     p.add_argument("--repeats", type=int, default=5)
     args = p.parse_args(argv)
 

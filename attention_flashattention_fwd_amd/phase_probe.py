@@ -234,7 +234,7 @@ def main(argv=None) -> int:
     p.add_argument("workloads", nargs="*",
                    default=["t16384_d128", "t4096_outliers", "t2048", "t2048_full"])
     p.add_argument("--build", action="store_true", help="build the instrumented library only")
-    p.add_argument("--out", default=str(ROOT / "gpurun_out" / "phase_probe.json"))
+    p.add_argument("--out", default="phase_probe.json", help="JSON report (default: ./phase_probe.json)")
     args = p.parse_args(argv)
     if args.build:
         build()
