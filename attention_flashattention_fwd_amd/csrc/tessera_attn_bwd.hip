@@ -609,35 +609,54 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
             ++f_g;
         }
     };
-    auto store = [&](int step) __attribute__((always_inline)) {
-        const int b3 = step % 3;
-        qs_.store((LDS_AS char *)lds_q[b3], tid);
-        ds_.store((LDS_AS char *)lds_d[step & 1], tid);
+    // Buffers of step s: Q tile, lse and Delta in [s % 3], dO tile and P in
+    // [s % 2].  The step loops below are unrolled by six, so every buffer index
+    // is a compile-time constant and each LDS read takes its buffer's base as
+    // an immediate offset instead of adding it per read.
+    auto store = [&]<int B3, int B2>() __attribute__((always_inline)) {
+        qs_.store((LDS_AS char *)lds_q[B3], tid);
+        ds_.store((LDS_AS char *)lds_d[B2], tid);
         if (tid < kTileRows) {
-            lds_l[b3][tid] = l_in;
-            lds_m[b3][tid] = m_in;
+            lds_l[B3][tid] = l_in;
+            lds_m[B3][tid] = m_in;
         }
     };
 
     fetch();
-    store(0);
+    store.template operator()<0, 0>();
     __syncthreads();
     // Each role runs its own loop (registers are allocated per role); both
     // pass the same barriers, one per step, and share the tile staging.
-    auto step_end = [&](int step) __attribute__((always_inline)) {
-        if (step + 1 < nsteps) store(step + 1);
+    auto step_end = [&]<int B3, int B2>(int step) __attribute__((always_inline)) {
+        if (step + 1 < nsteps) store.template operator()<(B3 + 1) % 3, B2 ^ 1>();
         __syncthreads();
+    };
+    // Runs step, step + 1, ... up to nsteps (inclusive), six per pass.
+    auto run_steps = [&](auto &&one) __attribute__((always_inline)) {
+        for (int step = 0; step <= nsteps; step += 6) {
+            one.template operator()<0, 0>(step);
+            if (step + 1 > nsteps) break;
+            one.template operator()<1, 1>(step + 1);
+            if (step + 2 > nsteps) break;
+            one.template operator()<2, 0>(step + 2);
+            if (step + 3 > nsteps) break;
+            one.template operator()<0, 1>(step + 3);
+            if (step + 4 > nsteps) break;
+            one.template operator()<1, 0>(step + 4);
+            if (step + 5 > nsteps) break;
+            one.template operator()<2, 1>(step + 5);
+        }
     };
     if (!dk_wave) {
         int c_qi = 0;   // query tile of the current step, counted like f_qi
-        for (int step = 0; step <= nsteps; ++step) {
+        auto dv_step = [&]<int B3, int B2>(int step) __attribute__((always_inline)) {
             if (step + 1 < nsteps) fetch();
             if (step < nsteps) {
                 const int q0 = (qt_first + c_qi) * kTileRows;
                 if (++c_qi == per_head) c_qi = 0;
                 const bool need_mask = causal && q0 < kw0 + 31;
-                const LDS_AS char *qt = (const LDS_AS char *)lds_q[step % 3];
-                const LDS_AS char *dt = (const LDS_AS char *)lds_d[step & 1];
+                const LDS_AS char *qt = (const LDS_AS char *)lds_q[B3];
+                const LDS_AS char *dt = (const LDS_AS char *)lds_d[B2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     // register i holds query row q0 + 32 h + 8 (i / 4) + 4 hi + i % 4
@@ -645,12 +664,12 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
 #pragma unroll
                     for (int ks = 0; ks < D / 16; ++ks)
                         sp = mfma32(read_row<D>(qt, off, h, ks), kv[ks], sp);
-                    f32x4 (&xp)[4][64] = lds_p[step & 1][h][w & 3];
+                    f32x4 (&xp)[4][64] = lds_p[B2][h][w & 3];
                     // exponent of P, masked in one branch per step (as above)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const f32x4 l4 =
-                            *(const LDS_AS f32x4 *)&lds_l[step % 3][32 * h + 8 * j + 4 * hi];
+                            *(const LDS_AS f32x4 *)&lds_l[B3][32 * h + 8 * j + 4 * hi];
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
                             sp[4 * j + u] = __builtin_fmaf(sp[4 * j + u], c, -l4[u]);
@@ -680,24 +699,25 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
                     }
                 }
             }
-            step_end(step);
-        }
+            step_end.template operator()<B3, B2>(step);
+        };
+        run_steps(dv_step);
     } else {
         f32x16 dp[2];   // dP of the step before (both halves)
-        for (int step = 0; step <= nsteps; ++step) {
+        auto dk_step = [&]<int B3, int B2>(int step) __attribute__((always_inline)) {
             if (step + 1 < nsteps) fetch();
             if (step > 0) {
                 // dS and dk of the step before: its Q tile, Delta and P are still in LDS
-                const int prev = step - 1;
-                const LDS_AS char *qt = (const LDS_AS char *)lds_q[prev % 3];
+                constexpr int P3 = (B3 + 2) % 3, P2 = B2 ^ 1;
+                const LDS_AS char *qt = (const LDS_AS char *)lds_q[P3];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const f32x4 (&xp)[4][64] = lds_p[prev & 1][h][w & 3];
+                    const f32x4 (&xp)[4][64] = lds_p[P2][h][w & 3];
                     f32x16 ds;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int r = 32 * h + 8 * j + 4 * hi;
-                        const f32x4 m4 = *(const LDS_AS f32x4 *)&lds_m[prev % 3][r];
+                        const f32x4 m4 = *(const LDS_AS f32x4 *)&lds_m[P3][r];
                         const f32x4 p4 = *(const LDS_AS f32x4 *)&xp[j][lane];
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
@@ -715,7 +735,7 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
                 }
             }
             if (step < nsteps) {
-                const LDS_AS char *dt = (const LDS_AS char *)lds_d[step & 1];
+                const LDS_AS char *dt = (const LDS_AS char *)lds_d[B2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     dp[h] = f32x16{};
@@ -724,8 +744,9 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
                         dp[h] = mfma32(read_row<D>(dt, off, h, ks), kv[ks], dp[h]);
                 }
             }
-            step_end(step);
-        }
+            step_end.template operator()<B3, B2>(step);
+        };
+        run_steps(dk_step);
     }
     if (key < T) {
         if (dk_wave) store_rows<D>(a.dk + ((int64_t)bh * T + key) * D, acc, a.scale, hi);
