@@ -8,6 +8,7 @@ a GPU, these functions raise.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 from pathlib import Path
@@ -16,6 +17,8 @@ import numpy as np
 
 PKG = Path(__file__).resolve().parent
 LIBRARY = PKG / "libtessera_attn.so"
+# The LDS-poisoned debug build of the same sources (tests only; see build.py).
+POISON_LIBRARY = PKG / "libtessera_attn_poison.so"
 
 # status codes (enum tessera_attn_status)
 OK = 0
@@ -52,55 +55,73 @@ class TileConfig(ctypes.Structure):
         return ("TileConfig(heads_per_workgroup={}, query_rows_per_wave={}, "
                 "workgroups_per_cu={}, persistent={})".format(*self.as_tuple()))
 
-_lib = None
+_libs: dict[Path, ctypes.CDLL] = {}
+_active = LIBRARY
 
 
 def library_path() -> Path:
-    return LIBRARY
+    return _active
+
+
+def _load(path: Path) -> ctypes.CDLL:
+    if not path.exists():
+        raise RuntimeError(
+            f"{path} is missing: build it with "
+            "`python -m attention_flashattention_fwd_amd.build` (needs ROCm hipcc)")
+    L = ctypes.CDLL(str(path))
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    sig = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.tessera_attn_fwd.argtypes = sig
+    L.tessera_attn_fwd.restype = i
+    L.tessera_attn_fwd_f32.argtypes = sig
+    L.tessera_attn_fwd_f32.restype = i
+    L.tessera_attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    L.tessera_attn_fwd_kv.restype = i
+    L.tessera_attn_bwd.argtypes = [vp] * 10 + [i] * 6 + [f, vp]
+    L.tessera_attn_bwd.restype = i
+    L.tessera_rmsnorm_fwd.argtypes = [vp, vp, vp, ctypes.c_longlong, i, f, vp]
+    L.tessera_rmsnorm_fwd.restype = i
+    L.tessera_paged_decode.argtypes = [vp] * 7 + [i] * 9 + [f, vp, ctypes.c_longlong, vp]
+    L.tessera_paged_decode.restype = i
+    L.tessera_paged_decode_workspace.argtypes = [i] * 7
+    L.tessera_paged_decode_noalloc.argtypes = [vp] * 7 + [i] * 9 + [f, vp]
+    L.tessera_paged_decode_noalloc.restype = i
+    L.tessera_attn_fwd_tile_config.argtypes = [i] * 7 + [ctypes.POINTER(TileConfig)]
+    L.tessera_attn_fwd_tile_config.restype = i
+    L.tessera_attn_fwd_with_config.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
+                                               ctypes.POINTER(TileConfig), vp]
+    L.tessera_attn_fwd_with_config.restype = i
+    L.tessera_paged_decode_scratch_limit.argtypes = []
+    L.tessera_paged_decode_scratch_limit.restype = ctypes.c_longlong
+    L.tessera_paged_decode_workspace.restype = ctypes.c_longlong
+    L.tessera_attn_status_string.argtypes = [i]
+    L.tessera_attn_status_string.restype = ctypes.c_char_p
+    L.tessera_attn_last_error.argtypes = []
+    L.tessera_attn_last_error.restype = ctypes.c_char_p
+    L.tessera_attn_version.argtypes = []
+    L.tessera_attn_version.restype = i
+    return L
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded HIP library; raises if it has not been built."""
-    global _lib
-    if _lib is None:
-        if not LIBRARY.exists():
-            raise RuntimeError(
-                f"{LIBRARY} is missing: build it with "
-                "`python -m attention_flashattention_fwd_amd.build` (needs ROCm hipcc)")
-        L = ctypes.CDLL(str(LIBRARY))
-        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-        sig = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
-        L.tessera_attn_fwd.argtypes = sig
-        L.tessera_attn_fwd.restype = i
-        L.tessera_attn_fwd_f32.argtypes = sig
-        L.tessera_attn_fwd_f32.restype = i
-        L.tessera_attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
-        L.tessera_attn_fwd_kv.restype = i
-        L.tessera_attn_bwd.argtypes = [vp] * 10 + [i] * 6 + [f, vp]
-        L.tessera_attn_bwd.restype = i
-        L.tessera_rmsnorm_fwd.argtypes = [vp, vp, vp, ctypes.c_longlong, i, f, vp]
-        L.tessera_rmsnorm_fwd.restype = i
-        L.tessera_paged_decode.argtypes = [vp] * 7 + [i] * 9 + [f, vp, ctypes.c_longlong, vp]
-        L.tessera_paged_decode.restype = i
-        L.tessera_paged_decode_workspace.argtypes = [i] * 7
-        L.tessera_paged_decode_noalloc.argtypes = [vp] * 7 + [i] * 9 + [f, vp]
-        L.tessera_paged_decode_noalloc.restype = i
-        L.tessera_attn_fwd_tile_config.argtypes = [i] * 7 + [ctypes.POINTER(TileConfig)]
-        L.tessera_attn_fwd_tile_config.restype = i
-        L.tessera_attn_fwd_with_config.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
-                                                   ctypes.POINTER(TileConfig), vp]
-        L.tessera_attn_fwd_with_config.restype = i
-        L.tessera_paged_decode_scratch_limit.argtypes = []
-        L.tessera_paged_decode_scratch_limit.restype = ctypes.c_longlong
-        L.tessera_paged_decode_workspace.restype = ctypes.c_longlong
-        L.tessera_attn_status_string.argtypes = [i]
-        L.tessera_attn_status_string.restype = ctypes.c_char_p
-        L.tessera_attn_last_error.argtypes = []
-        L.tessera_attn_last_error.restype = ctypes.c_char_p
-        L.tessera_attn_version.argtypes = []
-        L.tessera_attn_version.restype = i
-        _lib = L
-    return _lib
+    """The loaded HIP library (the production one unless use_library() says
+    otherwise); raises if it has not been built."""
+    if _active not in _libs:
+        _libs[_active] = _load(_active)
+    return _libs[_active]
+
+
+@contextlib.contextmanager
+def use_library(path: Path):
+    """Routes every call of this module through the HIP library at `path`
+    inside the block (the tests run the LDS-poisoned debug build this way).
+    Not thread-safe: the choice is module-wide."""
+    global _active
+    prev, _active = _active, Path(path)
+    try:
+        yield lib()
+    finally:
+        _active = prev
 
 
 def version() -> int:

@@ -1,5 +1,9 @@
 """Build the gfx950 HIP library in-tree: libtessera_attn.so beside this file
-(the attention forward and backward, paged decode, and the fused RMSNorm).
+(the attention forward and backward, paged decode, and the fused RMSNorm),
+and its LDS-poisoned debug build libtessera_attn_poison.so (the same sources
+with TESSERA_LDS_POISON defined: every kernel fills its LDS with a NaN
+pattern first, and every global->LDS load poisons its destination before it
+is issued, so a missing wait or barrier reads NaN; tests only).
 
     python -m attention_flashattention_fwd_amd.build
 """
@@ -17,6 +21,7 @@ SOURCES = [PKG / "csrc" / "tessera_attn.hip", PKG / "csrc" / "tessera_attn_bwd.h
            PKG / "csrc" / "tessera_rmsnorm.hip", PKG / "csrc" / "tessera_paged.hip"]
 INCLUDE = ROOT / "include"
 LIBRARY = PKG / "libtessera_attn.so"
+POISON_LIBRARY = PKG / "libtessera_attn_poison.so"
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -37,21 +42,35 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
+def _command(out: Path, extra: list[str]) -> list[str]:
+    return [hipcc(), *HIPCC_FLAGS, *extra, f"-I{INCLUDE}", *map(str, SOURCES), "-o", str(out)]
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> Path:
-    tmp = LIBRARY.with_suffix(".so.tmp")
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), f"-I{INCLUDE}", *map(str, SOURCES), "-o",
-           str(tmp)]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the fp32 feature flag and says so; drop that line
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIBRARY)
+    """Compiles both libraries (two hipcc processes side by side); returns the
+    production library's path."""
+    jobs = []
+    for lib, defs in ((LIBRARY, []), (POISON_LIBRARY, ["-DTESSERA_LDS_POISON"])):
+        tmp = lib.with_suffix(".so.tmp")
+        cmd = _command(tmp, [*defs, *(extra or [])])
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((lib, tmp, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                stderr=subprocess.PIPE, text=True)))
+    failed = []
+    for lib, tmp, proc in jobs:
+        _, stderr = proc.communicate()
+        # hipcc's host pass does not know the fp32 feature flag and says so; drop that line
+        noise = "is not a recognized feature for this target"
+        err = "\n".join(l for l in stderr.splitlines() if noise not in l)
+        if proc.returncode != 0:
+            failed.append(f"hipcc failed for {lib.name} ({proc.returncode}):\n{err}")
+            continue
+        if err.strip() and verbose:
+            print(err, file=sys.stderr)
+        os.replace(tmp, lib)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     return LIBRARY
 
 

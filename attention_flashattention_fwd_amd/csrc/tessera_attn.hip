@@ -23,6 +23,7 @@
 
 #include "tessera_attn.h"
 #include "launch.h"
+#include "lds_poison.h"
 
 #define TESSERA_VERSION 10200
 
@@ -141,6 +142,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+    lds_poison_lane16(lds);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(base), "s"(lds)
@@ -798,6 +800,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     static_assert(!PAIRED || (D <= 64 && !RAGGED), "two workgroups per CU: D <= 64, Tk % 64 == 0");
     static_assert(NQ == 1 || (D <= 64 && !PAIRED), "64 rows per wave: D <= 64, one workgroup per CU");
     __shared__ LdsRing<D> lds;
+    lds_poison_all();
     attn_fwd_bf16_item<D, RAGGED, PAIRED, NQ, false>(a, lds, (int)blockIdx.x);
 }
 
@@ -809,6 +812,7 @@ __attribute__((amdgpu_waves_per_eu(PAIRED ? 4 : 2)))
 attn_fwd_bf16_persistent_kernel(Bf16Args args) {
     __shared__ LdsRing<D> lds;
     __shared__ int s_item;
+    lds_poison_all();
 
     const int tid = threadIdx.x;
     uint32_t *const queue = args.queue;
@@ -875,6 +879,7 @@ attn_fwd_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
     constexpr int kPer = D / 4;
     __shared__ __attribute__((aligned(16))) float sk[kF32Keys * D];
     __shared__ __attribute__((aligned(16))) float sv[kF32Keys * D];
+    lds_poison_all();
 
     const int tid = threadIdx.x;
     const int sub = tid & 3;

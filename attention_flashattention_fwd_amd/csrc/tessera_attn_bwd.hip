@@ -37,6 +37,7 @@
 
 #include "tessera_attn.h"
 #include "launch.h"
+#include "lds_poison.h"
 
 
 namespace {
@@ -252,6 +253,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
     constexpr int kDqThreads = 64 * NW;
     __shared__ __attribute__((aligned(16))) char lds_k[2][Tile<D>::kBytes];
     __shared__ __attribute__((aligned(16))) char lds_v[2][Tile<D>::kBytes];
+    lds_poison_all();
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -393,6 +395,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     // P of one 32-row half from each dv wave to its dk wave: [half][pair][k][lane]
     // holds the lane's P registers 4k .. 4k+3.
     __shared__ __attribute__((aligned(16))) f32x4 lds_p[2][4][4][64];
+    lds_poison_all();
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -556,6 +559,7 @@ attn_bwd_dkdv_lag_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float lds_m[3][kTileRows];   // Delta
     // P of step s in [s % 2][half][pair][k][lane] (the lane's P registers 4k .. 4k+3)
     __shared__ __attribute__((aligned(16))) f32x4 lds_p[2][2][4][4][64];
+    lds_poison_all();
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

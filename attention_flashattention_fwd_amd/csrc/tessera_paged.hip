@@ -43,6 +43,7 @@
 
 #include "tessera_paged.h"
 #include "launch.h"
+#include "lds_poison.h"
 
 namespace {
 
@@ -138,6 +139,7 @@ __device__ __forceinline__ const char *uniform_ptr(const char *p) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+    lds_poison_lane16(lds);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :
                  : "v"(voff), "s"(uniform_ptr((const char *)base)), "s"(lds)
@@ -197,6 +199,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) pa
     constexpr int kKeysPerLoad = 64 / kCpr;
     static_assert((R - 1) * 2 * kLoads <= 63, "loads in flight exceed the vmcnt range");
     __shared__ __attribute__((aligned(16))) char lds[R][2][kTileBytes];
+    lds_poison_all();
 
     const int lane = threadIdx.x;
     const int col = lane & 31, hi = lane >> 5;

@@ -34,6 +34,16 @@ def test_library_loads_and_exports_every_symbol():
     assert binding.version() == 10200
 
 
+def test_poison_build_loads_and_exports_every_symbol():
+    # the LDS-poisoned debug build of the same sources
+    with binding.use_library(binding.POISON_LIBRARY) as lib:
+        for name in declared_functions():
+            assert hasattr(lib, name), name
+        assert binding.version() == 10200
+        assert call(B=0) == binding.ERR_SHAPE
+    assert binding.lib()._name == str(binding.LIBRARY)
+
+
 def test_status_strings():
     for code in range(0, 13):
         assert binding.status_string(code)

@@ -103,6 +103,32 @@ def test_paged_all_sequences_empty():
     assert np.all(o == 0.0) and np.all(np.isneginf(l))
 
 
+@pytest.mark.parametrize("D,bs", [(128, 16), (64, 32), (32, 48)])
+def test_paged_nan_in_rows_no_sequence_owns(D, bs):
+    """Cache rows that no sequence owns -- those past a sequence's length in
+    its last block, and the spare blocks -- hold NaN.  The kernel never reads
+    them, so the output equals the oracle's on the finite cache and the
+    kernel's own output with finite values there, bit for bit."""
+    lens = [1, 15, 17, 100, 333, 0, 1000]
+    q, kc, vc, table, cl = inputs.make_paged(7, 8, 2, 2, D, bs, context_lens=lens, spare=3,
+                                             seed=21 + D)
+    owned = torch.zeros((kc.shape[0], bs), dtype=torch.bool)
+    for b, n in enumerate(lens):
+        for t in range(n):
+            owned[int(table[b, t // bs]), t % bs] = True
+    assert (~owned).any()
+    kn, vn = kc.clone(), vc.clone()
+    for c in (kn, vn):
+        c.permute(0, 2, 1, 3)[~owned] = float("nan")
+    scale = inputs.default_scale(D)
+    say(f"case paged NaN outside the sequences D={D} bs={bs} unowned rows={int((~owned).sum())}")
+    o, l = run_paged(q, kn, vn, table, cl, True, scale)
+    O_ref, l_ref = reference(q, kc, vc, table, cl, True, scale)
+    check_paged(o, l, O_ref, l_ref, "NaN outside the sequences")
+    o2, l2 = run_paged(q, kc, vc, table, cl, True, scale)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
 def test_paged_bad_table_entry_and_length_give_nan():
     """A sequence with a table entry out of range, or a length past the
     table, gets NaN everywhere; the other sequences are unaffected."""
