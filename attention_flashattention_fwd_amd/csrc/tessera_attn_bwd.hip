@@ -310,14 +310,16 @@ attn_bwd_dq_kernel(BwdArgs a) {
     ks_.store((LDS_AS char *)lds_k[0], tid);
     vs_.store((LDS_AS char *)lds_v[0], tid);
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
+    // Tile t sits in buffer t % 2.  The loop below is unrolled by two, so the
+    // buffer index is a compile-time constant and each LDS read takes its
+    // buffer's base as an immediate offset.
+    auto one_tile = [&]<int CUR>(int t) __attribute__((always_inline)) {
         if (t + 1 < ntiles) {
             ks_.fetch(khead, (t + 1) * kTileRows, T, tid);
             vs_.fetch(vhead, (t + 1) * kTileRows, T, tid);
         }
-        const LDS_AS char *kt = (const LDS_AS char *)lds_k[cur];
-        const LDS_AS char *vt = (const LDS_AS char *)lds_v[cur];
+        const LDS_AS char *kt = (const LDS_AS char *)lds_k[CUR];
+        const LDS_AS char *vt = (const LDS_AS char *)lds_v[CUR];
         const int j0 = t * kTileRows;
         const bool masked = j0 + kTileRows > T || (causal && j0 + kTileRows - 1 > qw0);
         // The tile's keys in two 32-key halves (S, dP, dS and the dq update of
@@ -354,10 +356,14 @@ attn_bwd_dq_kernel(BwdArgs a) {
             }
         }
         if (t + 1 < ntiles) {
-            ks_.store((LDS_AS char *)lds_k[cur ^ 1], tid);
-            vs_.store((LDS_AS char *)lds_v[cur ^ 1], tid);
+            ks_.store((LDS_AS char *)lds_k[CUR ^ 1], tid);
+            vs_.store((LDS_AS char *)lds_v[CUR ^ 1], tid);
         }
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        one_tile.template operator()<0>(t);
+        if (t + 1 < ntiles) one_tile.template operator()<1>(t + 1);
     }
     if (query < T) store_rows<D>(a.dq + (qhead + query) * D, acc, a.scale, hi);
 }
