@@ -95,6 +95,7 @@ struct Bf16Args {
     int qmode;    // 0: q as given, 1: q negated (scale < 0), 2: q zeroed (scale == 0)
     float c;      // |scale| * log2(e)  (1 when scale == 0)
     int nitems;   // work items: query tiles x (KV head, head slot) pairs
+    int xcd_cus;  // compute units per XCD (the workgroup order of paired launches)
     uint32_t *queue;   // work queues of a persistent launch, or null (one item per workgroup)
 };
 
@@ -792,7 +793,24 @@ __device__ __forceinline__ void attn_fwd_bf16_item(Args &a, LdsRing<D> &lds, int
     }
 }
 
-// A plain launch: one workgroup per item, item blockIdx.x.
+// The item workgroup b of a two-workgroups-per-CU launch runs.  Workgroup b
+// goes to XCD b % 8, and workgroups j and j + C of one XCD (j = b / 8, C
+// compute units per XCD) start together on one CU and share it to the end,
+// as a probe of the hardware's placement showed.  Items come longest first,
+// so that second round is taken in reverse: the XCD's j-th longest item
+// shares its CU with its (2C - 1 - j)-th, and under the causal mask every CU
+// of a two-round grid gets the same number of tiles.  Later rounds go to the
+// CUs as they free up and keep the plain order.
+__device__ __forceinline__ int paired_item(int b, int nitems, int C) {
+    const int x = b & (kQueues - 1), j = b / kQueues;
+    if (j < C || j >= 2 * C) return b;
+    const int local = (nitems - x + kQueues - 1) / kQueues;   // items of XCD x
+    const int m = min(C, local - C);                          // of its second round
+    return (2 * C + m - 1 - j) * kQueues + x;
+}
+
+// A plain launch: one workgroup per item, item blockIdx.x (reordered as
+// above for two workgroups per CU).
 template <int D, bool RAGGED, bool PAIRED, int NQ>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(PAIRED ? 4 : 2)))
@@ -801,7 +819,8 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     static_assert(NQ == 1 || (D <= 64 && !PAIRED), "64 rows per wave: D <= 64, one workgroup per CU");
     __shared__ LdsRing<D> lds;
     lds_poison_all();
-    attn_fwd_bf16_item<D, RAGGED, PAIRED, NQ, false>(a, lds, (int)blockIdx.x);
+    const int item = PAIRED ? paired_item((int)blockIdx.x, a.nitems, a.xcd_cus) : (int)blockIdx.x;
+    attn_fwd_bf16_item<D, RAGGED, PAIRED, NQ, false>(a, lds, item);
 }
 
 // A persistent launch: each workgroup takes items from the queues until every
@@ -1087,6 +1106,8 @@ template <int D, bool RAGGED, bool PAIRED, int NQ>
 int launch_items(Bf16Args a, int64_t items, bool persistent, hipStream_t s) {
     a.nitems = (int)items;
     a.queue = nullptr;
+    a.xcd_cus = compute_units() / kQueues;
+    if (a.xcd_cus < 1) a.xcd_cus = 1;
     if constexpr (!PAIRED) {
         int cus = 0;
         uint32_t *q = persistent ? queue_block(s, &cus) : nullptr;
