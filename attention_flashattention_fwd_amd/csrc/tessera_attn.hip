@@ -884,10 +884,18 @@ attn_fwd_bf16_persistent_kernel(Bf16Args args) {
 
 // ---------------------------------------------------------------------------
 // fp32 kernel (vector ALUs): 64 query rows per workgroup, four lanes per row,
-// each lane owning D/4 interleaved dims; K/V tiles staged in LDS.
+// each lane owning D/4 consecutive dims; K/V tiles staged in LDS.  The online
+// softmax takes keys eight at a time: the eight scores are formed side by
+// side (independent dot products and lane exchanges), then one running-max
+// update, eight exponentials and one rescale of the accumulator serve them
+// all, so the loop is bound by issue rather than by one long dependency chain
+// per key.  Exponentials run in log2 units (exp2 of the score times
+// scale * log2 e), and lse is converted back to natural log at the end.
 // ---------------------------------------------------------------------------
 constexpr int kF32Rows = 64;
 constexpr int kF32Keys = 64;
+constexpr int kF32Block = 8;   // keys per softmax update
+constexpr float kLn2f = 0.693147180559945309f;
 
 template <int D>
 __global__ void __launch_bounds__(256)
@@ -895,7 +903,8 @@ attn_fwd_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
                     const float *__restrict__ v, float *__restrict__ out,
                     float *__restrict__ lse, int Hq, int Hkv, int T, int ntiles, int causal,
                     float scale) {
-    constexpr int kPer = D / 4;
+    constexpr int kPer = D / 4;     // dims per lane
+    constexpr int kVec = kPer / 4;  // ... as float4
     __shared__ __attribute__((aligned(16))) float sk[kF32Keys * D];
     __shared__ __attribute__((aligned(16))) float sv[kF32Keys * D];
     lds_poison_all();
@@ -909,14 +918,15 @@ attn_fwd_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
     const int i = tile * kF32Rows + (tid >> 2);
     const int64_t kv0 = ((int64_t)b * Hkv + h / (Hq / Hkv)) * T * D;
     const int64_t qrow = ((int64_t)bh * T + min(i, T - 1)) * D;
+    const float c2 = scale * (float)kLog2e;   // score -> log2 units
 
-    float qr[kPer], acc[kPer];
+    float4 qr[kVec], acc[kVec];
 #pragma unroll
-    for (int t = 0; t < kPer; ++t) {
-        qr[t] = q[qrow + sub + 4 * t];
-        acc[t] = 0.f;
+    for (int t = 0; t < kVec; ++t) {
+        qr[t] = *(const float4 *)(q + qrow + sub * kPer + 4 * t);
+        acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, l = 0.f;   // m in log2 units
 
     const int last_q = min(T, tile * kF32Rows + kF32Rows) - 1;
     const int kend = causal ? last_q + 1 : T;
@@ -934,28 +944,73 @@ attn_fwd_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
         }
         __syncthreads();
         const int jn = min(kF32Keys, kend - j0);
-        for (int jj = 0; jj < jn; ++jj) {
-            float part = 0.f;
+        for (int jb = 0; jb < jn; jb += kF32Block) {
+            float x[kF32Block];
 #pragma unroll
-            for (int t = 0; t < kPer; ++t) part += qr[t] * sk[jj * D + sub + 4 * t];
-            part += __shfl_xor(part, 1);
-            part += __shfl_xor(part, 2);
-            if (causal && j0 + jj > i) continue;   // same decision for the row's four lanes
-            const float s = part * scale;
-            const float mn = fmaxf(m, s);
-            const float alpha = expf(m - mn);
-            const float p = expf(s - mn);
-            l = l * alpha + p;
+            for (int u = 0; u < kF32Block; ++u) {
+                const float4 *kr = (const float4 *)(sk + (jb + u) * D + sub * kPer);
+                float part = 0.f;
 #pragma unroll
-            for (int t = 0; t < kPer; ++t) acc[t] = acc[t] * alpha + p * sv[jj * D + sub + 4 * t];
-            m = mn;
+                for (int t = 0; t < kVec; ++t) {
+                    const float4 kk = kr[t];
+                    part = fmaf(qr[t].x, kk.x, part);
+                    part = fmaf(qr[t].y, kk.y, part);
+                    part = fmaf(qr[t].z, kk.z, part);
+                    part = fmaf(qr[t].w, kk.w, part);
+                }
+                x[u] = part;
+            }
+#pragma unroll
+            for (int u = 0; u < kF32Block; ++u) x[u] += __shfl_xor(x[u], 1);
+#pragma unroll
+            for (int u = 0; u < kF32Block; ++u) x[u] += __shfl_xor(x[u], 2);
+            // keys past the tile's last visible key, and (causal) past this row, get -inf
+            float mb = m;
+#pragma unroll
+            for (int u = 0; u < kF32Block; ++u) {
+                const int kj = j0 + jb + u;
+                x[u] = (kj < kend && !(causal && kj > i)) ? x[u] * c2 : -INFINITY;
+                mb = fmaxf(mb, x[u]);
+            }
+            // a row with no visible key yet keeps l = 0 and acc = 0
+            const float mref = mb == -INFINITY ? 0.f : mb;
+            const float alpha = __builtin_amdgcn_exp2f(m - mref);
+            float ps = 0.f;
+#pragma unroll
+            for (int u = 0; u < kF32Block; ++u) {
+                x[u] = __builtin_amdgcn_exp2f(x[u] - mref);
+                ps += x[u];
+            }
+            l = fmaf(l, alpha, ps);
+#pragma unroll
+            for (int t = 0; t < kVec; ++t) {
+                float4 a4 = acc[t];
+                a4.x *= alpha;
+                a4.y *= alpha;
+                a4.z *= alpha;
+                a4.w *= alpha;
+#pragma unroll
+                for (int u = 0; u < kF32Block; ++u) {
+                    const float4 vv = *(const float4 *)(sv + (jb + u) * D + sub * kPer + 4 * t);
+                    a4.x = fmaf(x[u], vv.x, a4.x);
+                    a4.y = fmaf(x[u], vv.y, a4.y);
+                    a4.z = fmaf(x[u], vv.z, a4.z);
+                    a4.w = fmaf(x[u], vv.w, a4.w);
+                }
+                acc[t] = a4;
+            }
+            m = mb;
         }
     }
     if (i < T) {
         const float inv = 1.f / l;
 #pragma unroll
-        for (int t = 0; t < kPer; ++t) out[qrow + sub + 4 * t] = acc[t] * inv;
-        if (sub == 0) lse[(int64_t)bh * T + i] = m + logf(l);
+        for (int t = 0; t < kVec; ++t) {
+            const float4 a4 = acc[t];
+            *(float4 *)(out + qrow + sub * kPer + 4 * t) =
+                make_float4(a4.x * inv, a4.y * inv, a4.z * inv, a4.w * inv);
+        }
+        if (sub == 0) lse[(int64_t)bh * T + i] = m * kLn2f + logf(l);
     }
 }
 
