@@ -17,7 +17,8 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SOURCES = [PKG / "csrc" / "tessera_attn.hip", PKG / "csrc" / "tessera_attn_bwd.hip",
+SOURCES = [PKG / "csrc" / "tessera_attn.hip", PKG / "csrc" / "tessera_attn_f32.hip",
+           PKG / "csrc" / "tessera_attn_bwd.hip",
            PKG / "csrc" / "tessera_rmsnorm.hip", PKG / "csrc" / "tessera_paged.hip"]
 INCLUDE = ROOT / "include"
 LIBRARY = PKG / "libtessera_attn.so"

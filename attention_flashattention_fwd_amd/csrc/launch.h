@@ -15,6 +15,15 @@
 // tessera_attn.hip.
 __attribute__((visibility("hidden"))) int tessera_launch_result(hipError_t e);
 
+// Checks the arguments of a forward entry point (pointers, sizes, causal,
+// scale, alignment, aliasing of out and lse with the inputs; `elem` is the
+// element size in bytes) and returns TESSERA_OK or the status to return.
+// Defined in tessera_attn.hip.
+__attribute__((visibility("hidden"))) int
+tessera_validate_fwd(const void *q, const void *k, const void *v, const void *out, const void *lse,
+                     int B, int Hq, int Hkv, int Tq, int Tk, int D, int causal, float scale,
+                     size_t elem);
+
 // Launches `kernel` on `stream` with no dynamic LDS.  Each argument is
 // converted to the kernel's parameter type and held here until
 // hipLaunchKernel has copied it.
