@@ -224,6 +224,32 @@ def test_every_tile_configuration(D, T, causal, cfg):
     check_close(o, l, *refs[causal], "bf16", f"D={D} T={T} causal={causal} config={cfg}")
 
 
+# Two workgroups per CU take the second round of each XCD's workgroups in
+# reverse.  These grids give the XCDs between one and two rounds (32 and 64
+# workgroups on 32 CUs), uneven across the XCDs when the item count is not a
+# multiple of 8, so the reversed round is partial; every element is compared.
+@pytest.mark.parametrize("B,T,causal", [(6, 2048, True), (5, 1984, True), (5, 1984, False),
+                                        (3, 4032, True)])
+def test_paired_launch_with_a_partial_second_round(B, T, causal):
+    Hq, Hkv, D = 8, 2, 64
+    items = (T // 64) * B * Hkv
+    assert 8 * 32 < items < 8 * 64, items
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, T, D, "bf16", seed=B + T)
+    scale = inputs.default_scale(D)
+    say(f"case paired partial round B={B} T={T} causal={causal} items={items}")
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    out = torch.empty_like(qd)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    binding.attn_fwd_with_config_into(qd, kd, vd, out, lse, binding.TileConfig(4, 32, 2, 0),
+                                      causal)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    O_ref, l_ref = oracle.attn_fwd(inputs.bits(q), inputs.bits(k), inputs.bits(v), causal, scale)
+    check_close(o, l, O_ref, l_ref, "bf16", f"paired B={B} T={T} causal={causal}")
+
+
 def test_tile_configurations_the_sizes_do_not_allow():
     q, k, v = (t.cuda() for t in inputs.make_qkv(1, 12, 4, 100, 128, "bf16", seed=1))
     out = torch.empty_like(q)
