@@ -29,7 +29,7 @@ constexpr uint32_t kLdsPoison = 0xFFFFFFFFu;
 // LDS, so static LDS is all there is, from address 0).
 __device__ __forceinline__ void lds_poison_all() {
     const uint32_t bytes = __builtin_amdgcn_groupstaticsize();
-    for (uint32_t b = threadIdx.x * 4; b < bytes; b += blockDim.x * 4)
+    for (uint32_t b = threadIdx.x * 4; b + 4 <= bytes; b += blockDim.x * 4)
         asm volatile("ds_write_b32 %0, %1" : : "v"(b), "v"(kLdsPoison) : "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
     __syncthreads();
