@@ -647,6 +647,34 @@ __device__ __forceinline__ void attn_fwd_bf16_item(Args &a, LdsRing<D> &lds, int
             }
             return fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])) * c;
         };
+        // The two-workgroups-per-CU build (128 registers) forms P straight from
+        // the scores into the packed operand, two values of each block at a
+        // time, so that no fp32 copy of the tile sits beside the scores, which
+        // the OR test keeps live; its raise recomputes P the same way.
+        auto sweep_pack = [&](float m_sub) __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float a0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[nb][2 * e], c, -m_sub));
+                const float a1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[nb][2 * e + 1], c, -m_sub));
+                const float b0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[nb][2 * e], c, -m_sub));
+                const float b1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[nb][2 * e + 1], c, -m_sub));
+                pu[nb][e >> 2][e & 3] =
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a0, a1}, bf16x2));
+                pu[nb][2 + (e >> 2)][e & 3] =
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){b0, b1}, bf16x2));
+            }
+        };
+        auto raise_packed = [&](float m_own) __attribute__((always_inline)) {
+            const float m_new = fmaxf(m_run[nb], max_with_partner(m_own) + (float)kHeadroom);
+            const float alpha =
+                (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - m_new);
+            lsum[nb][0] *= alpha;
+            lsum[nb][1] *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) acc[nb][db] *= alpha;
+            m_run[nb] = m_new;
+            sweep_pack(m_new == -INFINITY ? 0.f : m_new);
+        };
         auto raise = [&](float m_own) __attribute__((always_inline)) {
             const float m_new = fmaxf(m_run[nb], max_with_partner(m_own) + (float)kHeadroom);
             const float alpha =
@@ -658,16 +686,22 @@ __device__ __forceinline__ void attn_fwd_bf16_item(Args &a, LdsRing<D> &lds, int
             m_run[nb] = m_new;
             sweep(m_new == -INFINITY ? 0.f : m_new);
         };
-        if (first) {
+        if constexpr (PAIRED) {
+            // The same test as below, on P packed by sweep_pack.
+            if (first) {
+                raise_packed(own_max());
+            } else {
+                sweep_pack(m_run[nb]);
+                uint32_t any = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) any |= pu[nb][k][j];
+                if (__builtin_amdgcn_ballot_w64((any & 0x40004000u) != 0) != 0)
+                    raise_packed(own_max());
+            }
+        } else if (first) {
             raise(own_max());
-            pack();
-        } else if constexpr (PAIRED) {
-            // The OR test keeps the scores live beside the packed P, which the
-            // 128-register build cannot afford; it tests its own tile max
-            // instead, and the scores die in the sweep when no raise follows.
-            sweep(m_run[nb]);
-            const float m_own = own_max();
-            if (__builtin_amdgcn_ballot_w64(m_own >= m_run[nb] + 1.f) != 0) raise(m_own);
             pack();
         } else {
             sweep(m_run[nb]);
@@ -715,10 +749,19 @@ __device__ __forceinline__ void attn_fwd_bf16_item(Args &a, LdsRing<D> &lds, int
     auto vbuf = [&](int b) __attribute__((always_inline)) { return (LDS_AS char *)lds.v[b]; };
     auto finish = [&](int t, int kn, int vn, bool first) __attribute__((always_inline)) {
         phase_barrier();
-        if (t + 1 < ntiles) preload<D, 0>(kbuf(kn), vn * kTB, off, ring);
-        else preload<D, 2>(nullptr, vn * kTB, off, ring);
+        // The first operands of the next MFMA phase: read at the start of the
+        // vector phase, or, in the two-workgroups-per-CU build, at its end,
+        // so that they are not live beside the scores and P.
+        if constexpr (!PAIRED) {
+            if (t + 1 < ntiles) preload<D, 0>(kbuf(kn), vn * kTB, off, ring);
+            else preload<D, 2>(nullptr, vn * kTB, off, ring);
+        }
         softmax_phase(t, first);
         settle<NQ>(pu);
+        if constexpr (PAIRED) {
+            if (t + 1 < ntiles) preload<D, 0>(kbuf(kn), vn * kTB, off, ring);
+            else preload<D, 2>(nullptr, vn * kTB, off, ring);
+        }
         phase_barrier();
     };
     // Iteration t: K(t) in buffer kc, V(t-1) in vp; loads into kw, vw; the

@@ -64,8 +64,9 @@ PATCHES = [
      "        const uint32_t tb_ = (uint32_t)__builtin_amdgcn_s_memtime();\n"
      "        phase_barrier();\n"
      "        const uint32_t tc_ = (uint32_t)__builtin_amdgcn_s_memtime();"),
-    ("        softmax_phase(t, first);\n        settle<NQ>(pu);\n        phase_barrier();\n    };",
-     "        softmax_phase(t, first);\n        settle<NQ>(pu);\n"
+    ("            else preload<D, 2>(nullptr, vn * kTB, off, ring);\n        }\n"
+     "        phase_barrier();\n    };",
+     "            else preload<D, 2>(nullptr, vn * kTB, off, ring);\n        }\n"
      "        const uint32_t td_ = (uint32_t)__builtin_amdgcn_s_memtime();\n"
      "        phase_barrier();\n"
      "        if (t >= 2 && t + 2 < ntiles) { pm += tb_ - ta; pv += td_ - tc_; pt += 1; }\n    };"),
