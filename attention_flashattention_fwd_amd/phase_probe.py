@@ -11,7 +11,8 @@ then runs it on forward workloads and reports, from the GPU's own clocks:
     MFMA phases and of its vector (softmax) phases, separately for the
     leading and the lagging wave of each SIMD;
   * per XCD: the last end, the earliest CU end and microseconds per tile, which
-    show how evenly the dies share the work;
+    show how evenly the dies share the work; per compute unit: its items, key
+    tiles and last end;
   * a least-squares fit of item duration = fixed part + tiles x per-tile part
     (the fixed part is what an item's start and end cost), and the spread of
     the items' starts and ends over the launch.
@@ -153,6 +154,19 @@ def analyse(rec: np.ndarray, items: int) -> dict:
                         "last_end_us": max(ends), "first_cu_end_us": min(ends),
                         "us_per_tile": float(np.median(dur / np.maximum(tiles[s], 1)))})
     out["per_xcd"] = per_xcd
+    # per compute unit: how many items and key tiles it ran, and when its last
+    # item ended (shows how evenly a grid's workgroups share the CUs)
+    key_all = xcc * 256 + se_sh * 16 + cu
+    cus = np.unique(key_all)
+    cu_tiles = np.array([tiles[key_all == k].sum() for k in cus])
+    cu_items = np.array([(key_all == k).sum() for k in cus])
+    cu_end = np.array([(end[key_all == k].max() - t0) / 100.0 for k in cus])
+    out["cus"] = int(len(cus))
+    out["items_per_cu_min_max"] = [int(cu_items.min()), int(cu_items.max())]
+    out["tiles_per_cu_min_median_max"] = [int(cu_tiles.min()), float(np.median(cu_tiles)),
+                                          int(cu_tiles.max())]
+    out["cu_last_end_us_min_median_max"] = [float(cu_end.min()), float(np.median(cu_end)),
+                                            float(cu_end.max())]
     # item duration = fixed part + per-tile part (least squares over the items):
     # the fixed part is an item's start (Q, the first K/V tiles) and end
     dur_us = (end - start) / 100.0

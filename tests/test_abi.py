@@ -302,3 +302,40 @@ def test_phase_probe_instruments_the_current_kernel_source():
     text = phase_probe.instrumented_source(phase_probe.SOURCE.read_text())
     assert text.count("__builtin_amdgcn_s_memtime") == 4
     assert "tessera_probe_set" in text
+
+
+def test_phase_probe_analysis_of_synthetic_records():
+    """The probe's summary on hand-made records: 4 items on 2 CUs of 2 XCDs,
+    item i with 10 (i + 1) tiles, start 0 and duration 5 + 2 x tiles us
+    (timestamps at 100 MHz), steady-state phase cycles 300 / 200 per tile."""
+    import numpy as np
+
+    from attention_flashattention_fwd_amd import phase_probe
+    items = 4
+    rec = np.zeros((items, 8, phase_probe.WORDS), dtype=np.uint32)
+    for it in range(items):
+        tiles = 10 * (it + 1)
+        cu, xcd = it % 2, it // 2          # items 0, 2 share CU 0; 1, 3 CU 1
+        start = 0 if it < 2 else 100 * (5 + 2 * 10 * (it - 1))   # second item after the first
+        end = start + 100 * (5 + 2 * tiles)
+        for w in range(8):
+            rec[it, w, 0] = (cu << 8)       # HW_ID: CU id, SH 0, SE 0
+            rec[it, w, 8] = 0               # every item on XCD 0 here
+            rec[it, w, 1], rec[it, w, 2] = start, 0
+            rec[it, w, 3], rec[it, w, 4] = end, 0
+            steady = tiles - 4
+            rec[it, w, 5] = 300 * steady
+            rec[it, w, 7] = 200 * steady
+            rec[it, w, 9] = steady | (tiles << 16)
+    out = phase_probe.analyse(rec, items)
+    assert out["items"] == 4 and out["cus"] == 2
+    assert abs(out["item_fixed_us"] - 5.0) < 1e-9 and abs(out["item_us_per_tile"] - 2.0) < 1e-9
+    assert out["leading_mfma_phase_cycles_per_tile"] == 300.0
+    assert out["lagging_vector_phase_cycles_per_tile"] == 200.0
+    assert out["items_per_cu_min_max"] == [2, 2]
+    assert out["tiles_per_cu_min_median_max"] == [40, 50.0, 60]   # 10 + 30, 20 + 40
+    ends = [e for e in out["cu_last_end_us_min_median_max"]]
+    # CU 0: item 2 starts at 25 us (after item 0's 5 + 20), ends at 25 + 65 = 90
+    # CU 1: item 3 starts at 45 us, ends at 45 + 85 = 130
+    assert abs(ends[0] - 90.0) < 1e-9 and abs(ends[2] - 130.0) < 1e-9
+    assert abs(out["span_us"] - 130.0) < 1e-9
