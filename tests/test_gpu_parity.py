@@ -351,6 +351,32 @@ def test_scale_values(dtype, scale):
     full_case(2, 8, 2, 150, 64, dtype, True, scale=scale, seed=7)
 
 
+# Large scales make every row sharply peaked and the running max rise many
+# times along a row (a raise needs a score about 33 / (scale log2 e) above the
+# max so far), which exercises the rescaling path of every build: the default
+# pick and two workgroups per CU (D = 64, whole key tiles).
+@pytest.mark.parametrize("scale", [8.0, -8.0, 30.0])
+@pytest.mark.parametrize("cfg", [None, (4, 32, 2, 0)])
+def test_large_scales(scale, cfg):
+    B, Hq, Hkv, T, D = 2, 8, 2, 1024, 64
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, T, D, "bf16", seed=11)
+    say(f"case large scale={scale} config={cfg}")
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    if cfg is None:
+        out, lse = binding.attn_fwd(qd, kd, vd, causal=True, scale=scale)
+    else:
+        out = torch.empty_like(qd)
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+        binding.attn_fwd_with_config_into(qd, kd, vd, out, lse, binding.TileConfig(*cfg), True,
+                                          scale)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    O_ref, l_ref = oracle.attn_fwd(inputs.bits(q), inputs.bits(k), inputs.bits(v), True, scale)
+    check_close(o, l, O_ref, l_ref, "bf16", f"scale={scale} config={cfg}")
+
+
 @pytest.mark.parametrize("mode", ["elements", "rows"])
 def test_outliers_small(mode):
     full_case(2, 8, 2, 600, 64, "bf16", True, seed=3, outliers=mode)
