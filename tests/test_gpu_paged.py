@@ -88,7 +88,7 @@ def test_paged_shapes(B, Hq, Hkv, Tq, D, bs, lens, causal):
 def test_paged_scale_sign_and_zero():
     q, kc, vc, table, cl = inputs.make_paged(3, 8, 2, 2, 64, 16, context_lens=[1, 40, 700],
                                              seed=11)
-    for scale in (-0.2, 0.0, 0.5):
+    for scale in (-0.2, 0.0, 0.5, 8.0, -8.0):
         say(f"case paged scale={scale}")
         o, l = run_paged(q, kc, vc, table, cl, True, scale)
         O_ref, l_ref = reference(q, kc, vc, table, cl, True, scale)
