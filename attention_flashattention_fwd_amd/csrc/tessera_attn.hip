@@ -487,8 +487,8 @@ __device__ __forceinline__ void mfma_phase(const LDS_AS char *kt, uint32_t vrel,
 // which is unrolled by four so every LDS buffer is a distinct array.
 // RAGGED: Tk % kKeyTile != 0 (the last key tile crosses Tk).
 // PAIRED: two workgroups per CU (four waves per SIMD, at most 128 VGPRs each;
-// D = 64 with Tk a multiple of the key tile only: the LDS ring is 64 KB, and
-// the ragged build would spill in the loop).  The two run independently, so the
+// D <= 64 with Tk a multiple of the key tile only: the LDS ring is at most
+// 64 KB, and the ragged build would spill in the loop).  The two run independently, so the
 // vector phases of one overlap the matrix-core phases of the other on top of
 // the ping-pong inside each: the vector work of a single wave is bound by its
 // own issue rate, and two waves issuing it side by side go about twice as fast.
