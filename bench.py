@@ -457,7 +457,7 @@ def main(argv=None):
             G = w.Hq // w.Hkv
             worst = 0.0
 
-            def judge(got, ref, top, sample_ref):
+            def bar_ratio(got, ref, top, sample_ref):
                 e = np.abs(got - ref)
                 rms = np.sqrt(np.mean(sample_ref * sample_ref))
                 return max(e.max() / (BWD_MAX * top), e.mean() / (BWD_MEAN * rms))
@@ -471,7 +471,7 @@ def main(argv=None):
                 work = 2.5 * w.flops * G / (w.B * w.Hq)
                 for got, ref in ((dq[:1, :G], rq), (dk[:1, :1], rk), (dv[:1, :1], rv)):
                     gv = got.float().cpu().numpy().astype(np.float64)
-                    worst = max(worst, judge(gv, ref, np.abs(ref).max(), ref))
+                    worst = max(worst, bar_ratio(gv, ref, np.abs(ref).max(), ref))
                 sample = (f"batch element 0, query heads 0..{G - 1} with KV head 0, all {w.T} "
                           f"rows ({work / 1e9:.1f} GFLOP counted as 2.5x the forward's")
                 where = "b=0, KV head 0, every element"
@@ -497,7 +497,7 @@ def main(argv=None):
                     top = float(f.abs().max())
                     idx = torch.from_numpy(rows).to(dev)
                     gv = (f.reshape(-1, w.D)[idx] if f.dim() == 4 else f.reshape(-1)[idx])
-                    worst = max(worst, judge(gv.cpu().numpy().astype(np.float64), ref, top, ref))
+                    worst = max(worst, bar_ratio(gv.cpu().numpy().astype(np.float64), ref, top, ref))
                 sample = (f"dq, Delta of {len(qrows)} random query rows and dk, dv of "
                           f"{len(krows)} random key rows of (b, KV head) {divmod(g0, w.Hkv)}, "
                           f"each from the definitions ({work / 1e9:.1f} GFLOP")
