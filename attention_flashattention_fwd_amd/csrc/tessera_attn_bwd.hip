@@ -16,7 +16,8 @@
 //     streams K and V tiles, forms S^T = K Q^T and dP^T = V dO^T on the
 //     matrix cores, P and dS on the vector ALUs, and dq^T += K^T dS^T.  It
 //     also writes Delta, from the dO and O rows it holds.
-//   * attn_bwd_dkdv_kernel (attn_bwd_dkdv_lag_kernel at D = 128): a
+//   * attn_bwd_dkdv_kernel (attn_bwd_dkdv_lag_kernel at D = 128, and at
+//     D <= 64 on grids of at most two workgroups per CU): a
 //     workgroup per 128-key tile of one KV head; it streams the Q and dO
 //     tiles of every query head of the group.  Two roles per key block: one
 //     wave forms S = Q K^T and P and accumulates dv^T += dO^T P, the other
@@ -548,11 +549,12 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
-// dk, dv at D = 128, with the hand-over of P one step late.  The roles are
-// those of attn_bwd_dkdv_kernel, but the dk wave forms dS and dk for step
-// s - 1 while the dv wave works on step s, so the P it reads was published
-// by the barrier that ends every step and no barrier is needed inside one
-// (at D = 128 one workgroup fills a CU, and nothing else hides those).  Q
+// dk, dv with the hand-over of P one step late (D = 128, and D <= 64 on grids
+// too small to give every CU a second workgroup).  The roles are those of
+// attn_bwd_dkdv_kernel, but the dk wave forms dS and dk for step s - 1 while
+// the dv wave works on step s, so the P it reads was published by the
+// barrier that ends every step and no barrier is needed inside one (with one
+// workgroup on a CU, nothing else hides those).  Q
 // tiles, lse and Delta therefore stay in LDS one step longer (three
 // buffers), P is double-buffered by step, and the loop runs one step past
 // the last tile for the dk wave.  Same arithmetic, in the same order.
@@ -769,6 +771,21 @@ bool overlaps(const void *x, size_t nx, const void *y, size_t ny) {
     return p < q + ny && q < p + nx;
 }
 
+// Up to this many dk/dv workgroups per compute unit, D <= 64 runs the
+// one-step-late build (one workgroup per CU, no barrier inside a step) rather
+// than the two-workgroups-per-CU build: measured on MI355X at D = 64 and 32,
+// 256 and 512 workgroups went 9-18 % faster, 1024 and 2048 went 4-16 % slower.
+constexpr int kLagGridPerCu = 2;
+
+int bwd_compute_units() {
+    int dev = -1, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n > 0)
+        return n;
+    return 256;   // MI355X
+}
+
 }  // namespace
 
 extern "C" int tessera_attn_bwd(const void *q, const void *k, const void *v, const void *out,
@@ -830,16 +847,23 @@ extern "C" int tessera_attn_bwd(const void *q, const void *k, const void *v, con
     hipStream_t s = (hipStream_t)stream;
     const dim3 g1((unsigned)grid_dq), b1(64 * a.dq_waves), g2((unsigned)grid_kv), b2(kKvThreads);
     // dq first: it writes the Delta rows the dk/dv kernel reads.
+    // dk/dv at D <= 64: the two-workgroups-per-CU build where the grid fills
+    // the second slots, else the one-step-late build (see there).
+    const bool lag = grid_kv <= kLagGridPerCu * (int64_t)bwd_compute_units();
     int st;
     if (D == 128) {
         st = tessera_launch(attn_bwd_dq_kernel<128>, g1, b1, s, a);
         if (st == TESSERA_OK) st = tessera_launch(attn_bwd_dkdv_lag_kernel<128>, g2, b2, s, a);
     } else if (D == 64) {
         st = tessera_launch(attn_bwd_dq_kernel<64>, g1, b1, s, a);
-        if (st == TESSERA_OK) st = tessera_launch(attn_bwd_dkdv_kernel<64>, g2, b2, s, a);
+        if (st == TESSERA_OK)
+            st = lag ? tessera_launch(attn_bwd_dkdv_lag_kernel<64>, g2, b2, s, a)
+                     : tessera_launch(attn_bwd_dkdv_kernel<64>, g2, b2, s, a);
     } else {
         st = tessera_launch(attn_bwd_dq_kernel<32>, g1, b1, s, a);
-        if (st == TESSERA_OK) st = tessera_launch(attn_bwd_dkdv_kernel<32>, g2, b2, s, a);
+        if (st == TESSERA_OK)
+            st = lag ? tessera_launch(attn_bwd_dkdv_lag_kernel<32>, g2, b2, s, a)
+                     : tessera_launch(attn_bwd_dkdv_kernel<32>, g2, b2, s, a);
     }
     return st;
 }

@@ -43,7 +43,11 @@ MAX_BAR = 2.0 ** -6
 MEAN_BAR = 2.0 ** -8
 
 # (B, Hq, Hkv, T, D, causal): N(0,1) shapes with GQA groups 1, 2, 3, 4, 5, 6,
-# 8 and 32, ragged T, causal and not; drawn by make_bwd with seed T + D.
+# 8 and 32, ragged T, causal and not; drawn by make_bwd with seed T + D.  The
+# last four have more than 512 dk/dv workgroups (one per KV head and 128-key
+# tile), two per CU on 256 CUs, so at D <= 64 they take the library's
+# two-workgroups-per-CU dk/dv build; the smaller grids take its one-step-late
+# build.
 BAR_CASES = [
     (1, 4, 2, 64, 64, True),       # one tile
     (2, 8, 2, 128, 128, True),
@@ -57,6 +61,10 @@ BAR_CASES = [
     (1, 16, 2, 200, 64, True),     # G = 8
     (2, 10, 2, 150, 128, False),   # G = 5, ragged, no mask
     (1, 32, 1, 96, 32, True),      # G = 32
+    (1, 80, 80, 900, 64, True),    # MHA, ragged: 640 dk/dv workgroups
+    (5, 192, 64, 130, 64, False),  # G = 3, ragged, no mask: 640
+    (3, 64, 32, 700, 32, True),    # ragged: 576
+    (10, 16, 16, 400, 32, False),  # MHA, no mask: 640
 ]
 
 

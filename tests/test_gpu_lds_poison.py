@@ -130,6 +130,22 @@ def test_poison_backward(D, T, causal):
     same(prod, pois, f"bwd D={D} T={T} causal={causal}")
 
 
+# 576 dk/dv workgroups (one per KV head and 128-key tile), more than two per
+# CU on 256 CUs: at D <= 64 the library runs its two-workgroups-per-CU dk/dv
+# build here, and the one-step-late build on the grids above.
+@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_poison_backward_large_grid(D, causal):
+    B, Hq, Hkv, T = 8, 16, 8, 1100
+    q, k, v = (t.to(DEV) for t in inputs.make_qkv(B, Hq, Hkv, T, D, "bf16", seed=T + D))
+    g = torch.Generator().manual_seed(T)
+    do = torch.randn((B, Hq, T, D), generator=g).to(torch.bfloat16).to(DEV)
+    out, lse = binding.attn_fwd(q, k, v, causal=causal)
+    say(f"case poison bwd large grid D={D} T={T} causal={causal}")
+    prod, pois = both(lambda: binding.attn_bwd(q, k, v, out, lse, do, causal=causal))
+    same(prod, pois, f"bwd large grid D={D} T={T} causal={causal}")
+
+
 _rng = np.random.default_rng(9)
 PAGED = [
     (9, 8, 2, 1, 128, 16, [1, 15, 16, 17, 100, 511, 512, 513, 3000], True),
