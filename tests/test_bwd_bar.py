@@ -99,3 +99,20 @@ def test_bar_follows_from_the_rounding_model():
     # the outlier slice is where the max-abs ratio peaks (dk: large q entries
     # weight many rounded dS terms)
     assert max(a for a, _ in rows[-1][1]) == worst_max
+
+
+def test_cases_cover_both_dkdv_builds_at_small_head_sizes():
+    # The library takes its one-step-late dk/dv build at D <= 64 on grids of at
+    # most two dk/dv workgroups (one per KV head and 128-key tile) per compute
+    # unit, its two-workgroups-per-CU build above: on the 256 CUs of an MI355X
+    # the boundary is 512.  The GPU cases must reach both builds at D = 64 and
+    # D = 32, causal or not among them.
+    def grid(case):
+        B, Hq, Hkv, T, D, causal = case
+        return B * Hkv * -(-T // 128)
+
+    for D in (32, 64):
+        small = [c for c in br.BAR_CASES if c[4] == D and grid(c) <= 2 * 256]
+        large = [c for c in br.BAR_CASES if c[4] == D and grid(c) > 2 * 256]
+        assert small and large, D
+        assert {c[5] for c in large} == {True, False}, D
