@@ -39,7 +39,7 @@ HEADLINE = "t16384_d128"
 # every other forward workload, each timed and checked against the oracle
 SECONDARY = ["t4096_outliers", "t4096_outlier_rows", "t2048", "t2048_full",
              "chunk2048_t16384_d128", "tiny_t128", "fp32_t64"]
-BACKWARD = ["t16384_d128", "t4096_outliers"]
+BACKWARD = ["t16384_d128", "t4096_outliers", "t2048"]
 KERNEL_SOURCE = ROOT / "attention_flashattention_fwd_amd" / "csrc" / "tessera_attn.hip"
 PROFILES = ROOT / "profiles"
 # Parity bars.  Forward: bf16 max-abs 2e-2 and mean-abs 2e-3 (O and lse
@@ -416,7 +416,8 @@ def main(argv=None):
         return 0
 
     def backward_lines():
-        """The attention backward on the long-context and T=4096 workloads.  Rate
+        """The attention backward on the long-context, T=4096 and T=2048 workloads
+        (the last a grid small enough for the one-step-late dk/dv build).  Rate
         counted the usual way, 2.5x the forward's flops (the five products S,
         dP, dq, dk, dv); the two kernels here execute seven (S and dP once in
         each).  The timed output is checked against the oracle: at T=4096 the
